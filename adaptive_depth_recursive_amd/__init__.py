@@ -1,0 +1,258 @@
+"""Python binding of libmor.so, the MI355X Mixture-of-Recursions library (include/mor.h).
+
+Argument marshalling only: every step of the forward pass runs in the HIP kernels behind the
+C ABI. PyTorch provides device memory and the stream. Importing this module does not load the
+library; the first call does, and fails loudly if it has not been built
+(``python -m adaptive_depth_recursive_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libmor.so")
+
+MOR_MAX_REC = 8
+MOR_OK, MOR_E_INVALID, MOR_E_SHAPE, MOR_E_WORKSPACE = 0, -1, -2, -3
+MOR_E_KV_FULL, MOR_E_HIP, MOR_E_STATE = -4, -5, -6
+MOR_F32, MOR_BF16 = 0, 1
+ROUTING = {"ec": 0, "tc": 1, "threshold": 2}
+KV_MODE = {"recursion": 0, "share": 1}
+GATE_MODE = {"router": 0, "unit": 1}
+DTYPE = {"f32": MOR_F32, "bf16": MOR_BF16}
+
+
+class MorError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"mor status {status}: {msg}")
+        self.status = status
+
+
+class mor_config(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+        ("n_layers", ctypes.c_int32), ("n_rec", ctypes.c_int32),
+        ("cap_num", ctypes.c_int32 * MOR_MAX_REC), ("cap_den", ctypes.c_int32),
+        ("routing", ctypes.c_int32), ("kv_mode", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+        ("max_batch", ctypes.c_int32), ("max_seq", ctypes.c_int32),
+    ]
+
+
+class mor_block_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "g_attn", "g_ffn")]
+
+
+class mor_weights(ctypes.Structure):
+    _fields_ = [("first", mor_block_weights), ("last", mor_block_weights),
+                ("shared", ctypes.POINTER(mor_block_weights)),
+                ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmor.so (raises if it is missing: there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m adaptive_depth_recursive_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.mor_abi_version.restype = i32
+        L.mor_last_error.restype = ctypes.c_char_p
+        L.mor_workspace_bytes.restype = sz
+        L.mor_workspace_bytes.argtypes = [ctypes.POINTER(mor_config)]
+        L.mor_init.restype = i32
+        L.mor_init.argtypes = [ctypes.POINTER(mor_config), ctypes.POINTER(mor_weights), vp, sz,
+                               vp, ctypes.POINTER(vp)]
+        L.mor_prefill.restype = i32
+        L.mor_prefill.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.mor_route.restype = i32
+        L.mor_route.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
+        L.mor_kv_view.restype = i32
+        L.mor_kv_view.argtypes = [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                  ctypes.POINTER(i32)]
+        L.mor_get_error_flags.restype = i32
+        L.mor_get_error_flags.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
+        L.mor_destroy.restype = None
+        L.mor_destroy.argtypes = [vp]
+        _lib = L
+    return _lib
+
+
+EXPORTED = ("mor_abi_version", "mor_last_error", "mor_workspace_bytes", "mor_init",
+            "mor_prefill", "mor_route", "mor_kv_view", "mor_get_error_flags", "mor_destroy")
+
+
+def _check(status: int):
+    if status != MOR_OK:
+        raise MorError(status, lib().mor_last_error().decode())
+
+
+def make_config(cfg, max_batch: Optional[int] = None, max_seq: Optional[int] = None) -> mor_config:
+    """A mor_config from any object with the workload configuration's attribute names."""
+    c = mor_config()
+    c.d_model, c.n_q_heads, c.n_kv_heads = cfg.d_model, cfg.n_q_heads, cfg.n_kv_heads
+    c.head_dim, c.d_ff, c.n_layers, c.n_rec = cfg.head_dim, cfg.d_ff, cfg.n_layers, cfg.n_rec
+    for i, v in enumerate(cfg.cap_num):
+        c.cap_num[i] = int(v)
+    c.cap_den = cfg.cap_den
+    c.routing, c.kv_mode = ROUTING[cfg.routing], KV_MODE[cfg.kv_mode]
+    c.gate_mode, c.dtype = GATE_MODE[cfg.gate_mode], DTYPE[cfg.dtype]
+    c.rms_eps, c.rope_theta = cfg.rms_eps, cfg.rope_theta
+    c.max_batch = cfg.batch if max_batch is None else max_batch
+    c.max_seq = cfg.seq if max_seq is None else max_seq
+    return c
+
+
+def workspace_bytes(c: mor_config) -> int:
+    n = lib().mor_workspace_bytes(ctypes.byref(c))
+    if n == 0:
+        raise MorError(MOR_E_INVALID, lib().mor_last_error().decode())
+    return n
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+class Mor:
+    """One initialised library handle with its device weights and workspace (torch tensors).
+
+    weights: {"first": layer, "shared": [layer], "last": layer, "router_w": [N_r][d],
+              "router_b": [N_r]} with [out][in] matrices (numpy or torch) and fp32 gains.
+    """
+
+    LAYER_KEYS = (("wq", "wq"), ("wk", "wk"), ("wv", "wv"), ("wo", "wo"), ("w_gate", "wg"),
+                  ("w_up", "wu"), ("w_down", "wd"), ("g_attn", "g_attn"), ("g_ffn", "g_ffn"))
+
+    def __init__(self, cfg, weights: Dict, device="cuda", max_batch=None, max_seq=None,
+                 stream=None):
+        import torch
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.c = make_config(cfg, max_batch, max_seq)
+        wdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        self._keep: List = []
+
+        def dev(x, dt):
+            t = torch.as_tensor(x).to(device=self.device, dtype=dt).contiguous()
+            self._keep.append(t)
+            return t
+
+        def block(layer):
+            bw = mor_block_weights()
+            for cname, key in self.LAYER_KEYS:
+                dt = torch.float32 if key.startswith("g_") else wdt
+                setattr(bw, cname, dev(layer[key], dt).data_ptr())
+            return bw
+
+        w = mor_weights()
+        w.first = block(weights["first"])
+        w.last = block(weights["last"])
+        shared = (mor_block_weights * max(1, len(weights["shared"])))()
+        for i, layer in enumerate(weights["shared"]):
+            shared[i] = block(layer)
+        w.shared = shared
+        w.router_w = dev(weights["router_w"], torch.float32).data_ptr()
+        rb = weights.get("router_b")
+        w.router_b = None if rb is None else dev(rb, torch.float32).data_ptr()
+        self.ws_bytes = workspace_bytes(self.c)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        h = ctypes.c_void_p()
+        _check(lib().mor_init(ctypes.byref(self.c), ctypes.byref(w), self.workspace.data_ptr(),
+                              self.ws_bytes, _stream(stream), ctypes.byref(h)))
+        self.handle = h
+        self._keep.clear()          # the library copied what it needs into the workspace
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().mor_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- calls -------------------------------------------------------------------------
+    def prefill(self, h_in, h_out=None, sel_pos=None, counts=None, logits=None, h_per_rec=None,
+                stream=None):
+        """mor_prefill on device tensors; h_in is fp32 [B, T, d]. Returns h_out."""
+        import torch
+        B, T, d = h_in.shape
+        if h_out is None:
+            h_out = torch.empty_like(h_in)
+        _check(lib().mor_prefill(self.handle, h_in.data_ptr(), B, T, h_out.data_ptr(),
+                                 _ptr(sel_pos), _ptr(counts), _ptr(logits), _ptr(h_per_rec),
+                                 _stream(stream)))
+        return h_out
+
+    def prefill_outputs(self, h_in, debug=True, stream=None):
+        """Prefill with every optional output allocated; returns a dict of device tensors."""
+        import torch
+        B, T, d = h_in.shape
+        R = self.cfg.n_rec
+        dev = h_in.device
+        out = {
+            "out": torch.empty_like(h_in),
+            "sel_pos": torch.empty((R, B, T), dtype=torch.int32, device=dev),
+            "counts": torch.empty((R, B), dtype=torch.int32, device=dev),
+            "logits": torch.empty((R, B, T), dtype=torch.float32, device=dev),
+            "h_per_rec": torch.empty((R + 1, B, T, d), dtype=torch.float32, device=dev) if debug else None,
+        }
+        self.prefill(h_in, out["out"], out["sel_pos"], out["counts"], out["logits"],
+                     out["h_per_rec"], stream)
+        return out
+
+    def route(self, H, active_in, counts_in, r, stream=None):
+        """mor_route: returns (active_out [B, T], counts_out [B], z [B, T])."""
+        import torch
+        B, T, _ = H.shape
+        act = torch.empty((B, T), dtype=torch.int32, device=H.device)
+        cnt = torch.empty((B,), dtype=torch.int32, device=H.device)
+        z = torch.empty((B, T), dtype=torch.float32, device=H.device)
+        _check(lib().mor_route(self.handle, H.data_ptr(), active_in.data_ptr(),
+                               counts_in.data_ptr(), r, B, T, act.data_ptr(), cnt.data_ptr(),
+                               z.data_ptr(), _stream(stream)))
+        return act, cnt, z
+
+    def kv_view(self, stream_index: int):
+        """(K device pointer, V^T device pointer, kpad) of one layer's cache."""
+        k, v = ctypes.c_void_p(), ctypes.c_void_p()
+        kpad = ctypes.c_int32()
+        _check(lib().mor_kv_view(self.handle, stream_index, ctypes.byref(k), ctypes.byref(v),
+                                 ctypes.byref(kpad)))
+        return k.value, v.value, kpad.value
+
+    def kv_tensors(self, stream_index: int, B: int):
+        """K [B, kpad, Hkv, hd] and V^T [B, Hkv, hd, kpad] as views into the workspace."""
+        import torch
+        k, v, kpad = self.kv_view(stream_index)
+        es = 2 if self.cfg.dtype == "bf16" else 4
+        dt = torch.bfloat16 if es == 2 else torch.float32
+        Hkv, hd = self.cfg.n_kv_heads, self.cfg.head_dim
+        base = self.workspace.data_ptr()
+        n = B * kpad * Hkv * hd
+        kt = self.workspace[k - base:k - base + n * es].view(dt).view(B, kpad, Hkv, hd)
+        vt = self.workspace[v - base:v - base + n * es].view(dt).view(B, Hkv, hd, kpad)
+        return kt, vt
+
+    def error_flags(self, stream=None) -> int:
+        f = ctypes.c_uint32()
+        _check(lib().mor_get_error_flags(self.handle, _stream(stream), ctypes.byref(f)))
+        return f.value

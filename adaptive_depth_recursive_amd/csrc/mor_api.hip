@@ -1,0 +1,475 @@
+// Host runtime behind include/mor.h: config validation, workspace plan, weight packing and the
+// enqueue order of the MoR prefill. Host code only; every step of the computation runs in the
+// kernels of k_gemm.hip, k_attn.hip and k_route.hip.
+//
+// Prefill order (MoR paper A.1-A.3; reading notes 1, 2.1-2.2, 3.1-3.2):
+//   first layer on all tokens -> router r=1
+//   for r = 1..N_r: select the active set, gather its rows, run the n_s shared layers on them
+//                   (attention over the tokens active at r, or over the recursion-1 tokens under
+//                   KV sharing), gated scatter back into H fused with the router of r+1
+//   last layer on all tokens.
+// Expert-choice counts are static, so nothing is read back to the host during a call.
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "mor.h"
+#include "mor_internal.h"
+
+using namespace mor;
+
+namespace {
+
+thread_local std::string g_err;
+
+mor_status fail(mor_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+#define HIPCHK(expr)                                                              \
+  do {                                                                            \
+    hipError_t e_ = (expr);                                                       \
+    if (e_ != hipSuccess)                                                         \
+      return fail(MOR_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_));  \
+  } while (0)
+
+struct BlockPacked {
+  void* wqkv;   // [(Hq + 2 Hkv) hd][d]: Wq rows, then Wk, then Wv
+  void* wo;     // [d][Hq hd]
+  void* wgu;    // [2 d_ff][d]: gate/up rows in alternating groups of 16
+  void* wd;     // [d][d_ff]
+  float* g_attn;
+  float* g_ffn;
+};
+
+constexpr size_t kAlign = 256;
+
+struct Cursor {
+  char* base;
+  size_t off = 0;
+  template <typename P>
+  P* take(size_t bytes) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    P* p = base ? reinterpret_cast<P*>(base + off) : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+}  // namespace
+
+struct mor_handle_s {
+  mor_config cfg;
+  int n_s = 0, es = 0, nq = 0, nkv = 0, nqkv = 0, kpad = 0, nstreams = 0;
+  size_t MT = 0;                 // max_batch * max_seq
+  std::vector<BlockPacked> blk;  // 0 = first, 1..n_s = shared, n_s + 1 = last
+  float* router_w = nullptr;
+  float* router_b = nullptr;
+  bool has_bias = false;
+  float* rope_cos = nullptr;
+  float* rope_sin = nullptr;
+  float* X = nullptr;
+  void* Xn = nullptr;
+  void* Q = nullptr;
+  void* O = nullptr;
+  void* Hf = nullptr;
+  char* kv = nullptr;
+  size_t kv_half_bytes = 0;      // bytes of K (= bytes of V^T) of one stream
+  int* act = nullptr;            // [N_r + 1][MT]   set r as [B][T] (positions, -1 padded)
+  int* cnt = nullptr;            // [N_r + 1][max_batch]
+  int* meta = nullptr;           // [N_r + 2][max_batch + 1]; the last slot is scratch
+  float* z = nullptr;            // [N_r + 1][MT]   z[r] by source row b*T + pos
+  float* tc_logits = nullptr;    // [N_r][MT]
+  int* depth = nullptr;          // [MT]
+  float* prob = nullptr;         // [MT]
+  int* rows_all = nullptr;       // 4 x [MT]: pos, src, seq, idx of the all-token set
+  int* rows = nullptr;           // 4 x [MT]: the same for the current active set
+  float* gate = nullptr;         // [MT]
+  unsigned* err = nullptr;
+};
+
+namespace {
+
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+mor_status validate(const mor_config* c) {
+  if (!c) return fail(MOR_E_INVALID, "null config");
+  if (c->dtype != MOR_F32 && c->dtype != MOR_BF16) return fail(MOR_E_INVALID, "dtype");
+  if (c->routing < 0 || c->routing > 2) return fail(MOR_E_INVALID, "routing");
+  if (c->kv_mode < 0 || c->kv_mode > 1) return fail(MOR_E_INVALID, "kv_mode");
+  if (c->gate_mode < 0 || c->gate_mode > 1) return fail(MOR_E_INVALID, "gate_mode");
+  if (c->d_model <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->d_ff <= 0 || c->n_layers < 3 || c->n_rec < 1 || c->n_rec > MOR_MAX_REC)
+    return fail(MOR_E_INVALID, "non-positive dimension or n_rec outside 1..8");
+  if ((c->n_layers - 2) % c->n_rec) return fail(MOR_E_INVALID, "(n_layers - 2) % n_rec != 0");
+  const int n_s = (c->n_layers - 2) / c->n_rec;
+  if (n_s > MOR_MAX_SHARED) return fail(MOR_E_SHAPE, "more than 64 shared layers");
+  if (c->d_model % 64 || c->d_ff % 64) return fail(MOR_E_SHAPE, "d_model and d_ff must be multiples of 64");
+  if (c->dtype == MOR_BF16 && c->head_dim != 64) return fail(MOR_E_SHAPE, "bf16 needs head_dim 64");
+  if (c->dtype == MOR_F32 && c->head_dim != 16 && c->head_dim != 32 && c->head_dim != 64)
+    return fail(MOR_E_SHAPE, "fp32 needs head_dim 16, 32 or 64");
+  if (c->n_q_heads % c->n_kv_heads || c->n_q_heads / c->n_kv_heads > 4)
+    return fail(MOR_E_SHAPE, "n_q_heads must be 1..4 times n_kv_heads");
+  if ((c->n_q_heads * c->head_dim) % 64) return fail(MOR_E_SHAPE, "n_q_heads * head_dim % 64 != 0");
+  if (c->cap_den <= 0) return fail(MOR_E_INVALID, "cap_den");
+  for (int r = 0; r < c->n_rec; ++r) {
+    if (c->cap_num[r] < 0 || c->cap_num[r] > c->cap_den) return fail(MOR_E_INVALID, "capacity outside [0, 1]");
+    if (r && c->cap_num[r] > c->cap_num[r - 1]) return fail(MOR_E_INVALID, "capacities must be non-increasing");
+  }
+  if (c->max_batch < 1 || c->max_seq < 1 || c->max_seq > 8192)
+    return fail(MOR_E_SHAPE, "max_batch >= 1 and 1 <= max_seq <= 8192");
+  if ((double)c->max_batch * c->max_seq * (double)std::max(c->d_ff, c->d_model) > 2.0e9)
+    return fail(MOR_E_SHAPE, "max_batch * max_seq too large");
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail(MOR_E_INVALID, "rms_eps / rope_theta");
+  return MOR_OK;
+}
+
+// Walks the workspace; with base == nullptr only sizes it.
+size_t plan(const mor_config& c, mor_handle_s* h, char* base) {
+  Cursor cur{base};
+  const int n_s = (c.n_layers - 2) / c.n_rec;
+  const size_t es = c.dtype == MOR_BF16 ? 2 : 4;
+  const size_t d = c.d_model, dff = c.d_ff, hd = c.head_dim;
+  const size_t nq = c.n_q_heads * hd, nkv = c.n_kv_heads * hd, nqkv = nq + 2 * nkv;
+  const size_t MT = (size_t)c.max_batch * c.max_seq;
+  const int R = c.n_rec;
+  const size_t kpad = (size_t)ceil_div(c.max_seq, 64) * 64;
+  const int nstreams = 2 + R * n_s;
+  std::vector<BlockPacked> blk(n_s + 2);
+  for (auto& b : blk) {
+    b.wqkv = cur.take<void>(nqkv * d * es);
+    b.wo = cur.take<void>(d * nq * es);
+    b.wgu = cur.take<void>(2 * dff * d * es);
+    b.wd = cur.take<void>(d * dff * es);
+    b.g_attn = cur.take<float>(d * 4);
+    b.g_ffn = cur.take<float>(d * 4);
+  }
+  float* router_w = cur.take<float>(R * d * 4);
+  float* router_b = cur.take<float>(R * 4);
+  float* rope_cos = cur.take<float>((size_t)c.max_seq * (hd / 2) * 4);
+  float* rope_sin = cur.take<float>((size_t)c.max_seq * (hd / 2) * 4);
+  float* X = cur.take<float>(MT * d * 4);
+  void* Xn = cur.take<void>(MT * d * es);
+  void* Q = cur.take<void>(MT * nq * es);
+  void* O = cur.take<void>(MT * nq * es);
+  void* Hf = cur.take<void>(MT * dff * es);
+  const size_t kv_half = (size_t)c.max_batch * kpad * nkv * es;
+  char* kv = cur.take<char>(kv_half * 2 * nstreams);
+  int* act = cur.take<int>((R + 1) * MT * 4);
+  int* cnt = cur.take<int>((R + 1) * (size_t)c.max_batch * 4);
+  int* meta = cur.take<int>((R + 2) * (size_t)(c.max_batch + 1) * 4);
+  float* z = cur.take<float>((R + 1) * MT * 4);
+  float* tc_logits = cur.take<float>(R * MT * 4);
+  int* depth = cur.take<int>(MT * 4);
+  float* prob = cur.take<float>(MT * 4);
+  int* rows_all = cur.take<int>(4 * MT * 4);
+  int* rows = cur.take<int>(4 * MT * 4);
+  float* gate = cur.take<float>(MT * 4);
+  unsigned* err = cur.take<unsigned>(64);
+  if (h) {
+    h->n_s = n_s; h->es = (int)es; h->nq = (int)nq; h->nkv = (int)nkv; h->nqkv = (int)nqkv;
+    h->kpad = (int)kpad; h->nstreams = nstreams; h->MT = MT;
+    h->blk = blk; h->router_w = router_w; h->router_b = router_b;
+    h->rope_cos = rope_cos; h->rope_sin = rope_sin;
+    h->X = X; h->Xn = Xn; h->Q = Q; h->O = O; h->Hf = Hf;
+    h->kv = kv; h->kv_half_bytes = kv_half;
+    h->act = act; h->cnt = cnt; h->meta = meta; h->z = z; h->tc_logits = tc_logits;
+    h->depth = depth; h->prob = prob; h->rows_all = rows_all; h->rows = rows; h->gate = gate;
+    h->err = err;
+  }
+  return cur.off + kAlign;
+}
+
+// ------------------------------------------------------------------ one decoder layer
+struct RowSet {
+  const int* meta;     // row-set descriptor
+  const int* cnt;      // [B] rows per sequence
+  const int* rows;     // 4 x [MT] pos/src/seq/idx
+  int m_upper;         // grid bound on the row count
+  int max_per_seq;     // grid bound on rows per sequence
+};
+struct KeySet {
+  const void* k;
+  const void* vt;
+  const int* kpos;     // [B][T]
+  const int* kcnt;     // [B]
+};
+
+template <typename E>
+mor_status run_layer(mor_handle_s* h, const BlockPacked& w, float* X, const RowSet& rs,
+                     void* k_dst, void* vt_dst, const KeySet& keys, int B, int T, hipStream_t s) {
+  const mor_config& c = h->cfg;
+  const int d = c.d_model, dff = c.d_ff, MT = (int)h->MT;
+  E* Xn = reinterpret_cast<E*>(h->Xn);
+  HIPCHK(launch_rmsnorm<E>(X, d, rs.meta, rs.m_upper, w.g_attn, c.rms_eps, Xn, s));
+
+  GemmEpi ep{};
+  ep.q = h->Q; ep.ldq = h->nq;
+  ep.k = k_dst; ep.vt = vt_dst;
+  ep.nq = h->nq; ep.nkv = h->nkv; ep.hd = c.head_dim; ep.hkv = c.n_kv_heads; ep.kpad = h->kpad;
+  ep.rowpos = rs.rows; ep.rowseq = rs.rows + 2 * (size_t)MT; ep.rowidx = rs.rows + 3 * (size_t)MT;
+  ep.rope_cos = h->rope_cos; ep.rope_sin = h->rope_sin;
+  const int n_qkv = k_dst ? h->nqkv : h->nq;
+  HIPCHK(launch_gemm<E>(EPI_QKV, Xn, reinterpret_cast<const E*>(w.wqkv), n_qkv, d, rs.m_upper, rs.meta, ep, s));
+
+  AttnArgs aa{};
+  aa.q = h->Q; aa.ldq = h->nq; aa.qmeta = rs.meta; aa.qcnt = rs.cnt; aa.qpos = rs.rows;
+  aa.k = keys.k; aa.vt = keys.vt; aa.kpos = keys.kpos; aa.ldkpos = T; aa.kcnt = keys.kcnt;
+  aa.kpad = h->kpad; aa.hkv = c.n_kv_heads; aa.hq = c.n_q_heads; aa.hd = c.head_dim;
+  aa.o = h->O; aa.ldo = h->nq;
+  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+  HIPCHK(launch_attention<E>(aa, B, rs.max_per_seq, s));
+
+  GemmEpi er{};
+  er.x = X; er.ldx = d;
+  HIPCHK(launch_gemm<E>(EPI_RESID, reinterpret_cast<const E*>(h->O), reinterpret_cast<const E*>(w.wo), d, h->nq, rs.m_upper, rs.meta, er, s));
+  HIPCHK(launch_rmsnorm<E>(X, d, rs.meta, rs.m_upper, w.g_ffn, c.rms_eps, Xn, s));
+  GemmEpi eg{};
+  eg.h = h->Hf; eg.ldh = dff;
+  HIPCHK(launch_gemm<E>(EPI_SWIGLU, Xn, reinterpret_cast<const E*>(w.wgu), 2 * dff, d, rs.m_upper, rs.meta, eg, s));
+  HIPCHK(launch_gemm<E>(EPI_RESID, reinterpret_cast<const E*>(h->Hf), reinterpret_cast<const E*>(w.wd), d, dff, rs.m_upper, rs.meta, er, s));
+  return MOR_OK;
+}
+
+void* kv_k(mor_handle_s* h, int stream) { return h->kv + (size_t)stream * 2 * h->kv_half_bytes; }
+void* kv_vt(mor_handle_s* h, int stream) { return h->kv + ((size_t)stream * 2 + 1) * h->kv_half_bytes; }
+
+template <typename E>
+mor_status prefill_impl(mor_handle_s* h, const float* h_in, int B, int T, float* H,
+                        int32_t* sel_pos, int32_t* counts, float* logits, float* h_per_rec,
+                        hipStream_t s) {
+  const mor_config& c = h->cfg;
+  const int R = c.n_rec, n_s = h->n_s, d = c.d_model;
+  const size_t MT = h->MT, BT = (size_t)B * T;
+  const size_t hbytes = BT * d * sizeof(float);
+  int ks[MOR_MAX_REC];
+  for (int r = 0; r < R; ++r) ks[r] = ceil_div((long)c.cap_num[r] * T, c.cap_den);
+
+  if (H != h_in) HIPCHK(hipMemcpyAsync(H, h_in, hbytes, hipMemcpyDeviceToDevice, s));
+  int* meta_r[MOR_MAX_REC + 2];
+  for (int r = 0; r <= R + 1; ++r) meta_r[r] = h->meta + (size_t)r * (c.max_batch + 1);
+  auto act_r = [&](int r) { return h->act + (size_t)r * MT; };
+  auto cnt_r = [&](int r) { return h->cnt + (size_t)r * c.max_batch; };
+  auto z_r = [&](int r) { return h->z + (size_t)r * MT; };
+  HIPCHK(launch_init_sets(B, T, act_r(0), cnt_r(0), meta_r[0], h->rows_all, h->rows_all + MT,
+                          h->rows_all + 2 * MT, h->rows_all + 3 * MT, s));
+  if (logits && c.routing != MOR_ROUTE_TOKEN_CHOICE)
+    HIPCHK(launch_fill_f32(h->z + MT, R * MT, NAN, s));
+
+  const RowSet all{meta_r[0], cnt_r(0), h->rows_all, (int)BT, T};
+  const KeySet keys_first{kv_k(h, 0), kv_vt(h, 0), act_r(0), cnt_r(0)};
+  mor_status st = run_layer<E>(h, h->blk[0], H, all, kv_k(h, 0), kv_vt(h, 0), keys_first, B, T, s);
+  if (st != MOR_OK) return st;
+  if (h_per_rec) HIPCHK(hipMemcpyAsync(h_per_rec, H, hbytes, hipMemcpyDeviceToDevice, s));
+
+  const bool tc = c.routing == MOR_ROUTE_TOKEN_CHOICE;
+  if (tc) {
+    HIPCHK(launch_router_tc(H, d, (int)BT, h->router_w, R, h->tc_logits, h->depth, h->prob, s));
+  } else {
+    HIPCHK(launch_router(H, d, h->rows_all + MT, meta_r[0], (int)BT, h->router_w,
+                         h->has_bias ? h->router_b : nullptr, z_r(1), s));
+  }
+  const int sel_mode = c.routing == MOR_ROUTE_EC_TOPK ? SEL_EC
+                       : c.routing == MOR_ROUTE_THRESHOLD ? SEL_THRESHOLD : SEL_TC;
+  const int gate_kind = c.gate_mode == MOR_GATE_UNIT ? GATE_ASSIGN : tc ? GATE_TC : GATE_SIGMOID;
+  for (int r = 1; r <= R; ++r) {
+    HIPCHK(launch_select(sel_mode, B, T, z_r(r), h->depth, act_r(r - 1), cnt_r(r - 1), ks[r - 1], r,
+                         act_r(r), cnt_r(r), h->err, s));
+    HIPCHK(launch_offsets(cnt_r(r), B, meta_r[r], s));
+    const int per_seq = sel_mode == SEL_EC ? std::min(ks[r - 1], T) : T;
+    const int m_up = B * per_seq;
+    HIPCHK(launch_gather(H, d, act_r(r), meta_r[r], B, T, m_up, gate_kind, z_r(r), h->depth,
+                         h->prob, r, h->X, h->rows, h->rows + MT, h->rows + 2 * MT, h->rows + 3 * MT,
+                         h->gate, s));
+    const RowSet rs{meta_r[r], cnt_r(r), h->rows, m_up, per_seq};
+    for (int j = 1; j <= n_s; ++j) {
+      const int sid = 1 + (r - 1) * n_s + (j - 1);
+      const bool share = c.kv_mode == MOR_KV_SHARE_FIRST && r >= 2;
+      if (share) {
+        const int s1 = 1 + (j - 1);
+        const KeySet ks1{kv_k(h, s1), kv_vt(h, s1), act_r(1), cnt_r(1)};
+        st = run_layer<E>(h, h->blk[j], h->X, rs, nullptr, nullptr, ks1, B, T, s);
+      } else {
+        const KeySet kr{kv_k(h, sid), kv_vt(h, sid), act_r(r), cnt_r(r)};
+        st = run_layer<E>(h, h->blk[j], h->X, rs, kv_k(h, sid), kv_vt(h, sid), kr, B, T, s);
+      }
+      if (st != MOR_OK) return st;
+    }
+    const float* w_next = (!tc && r < R) ? h->router_w + (size_t)r * d : nullptr;
+    const float* b_next = (w_next && h->has_bias) ? h->router_b + r : nullptr;
+    HIPCHK(launch_scatter(H, h->X, d, meta_r[r], m_up, h->rows + MT, h->gate, w_next, b_next,
+                          z_r(r + 1 <= R ? r + 1 : R), s));
+    if (h_per_rec)
+      HIPCHK(hipMemcpyAsync(h_per_rec + (size_t)r * BT * d, H, hbytes, hipMemcpyDeviceToDevice, s));
+  }
+  const int last = 1 + R * n_s;
+  const KeySet keys_last{kv_k(h, last), kv_vt(h, last), act_r(0), cnt_r(0)};
+  st = run_layer<E>(h, h->blk[n_s + 1], H, all, kv_k(h, last), kv_vt(h, last), keys_last, B, T, s);
+  if (st != MOR_OK) return st;
+
+  for (int r = 1; r <= R; ++r) {
+    if (sel_pos)
+      HIPCHK(hipMemcpyAsync(sel_pos + (size_t)(r - 1) * BT, act_r(r), BT * 4, hipMemcpyDeviceToDevice, s));
+    if (counts)
+      HIPCHK(hipMemcpyAsync(counts + (size_t)(r - 1) * B, cnt_r(r), (size_t)B * 4, hipMemcpyDeviceToDevice, s));
+  }
+  if (logits) {
+    if (tc) {
+      for (int r = 0; r < R; ++r)
+        HIPCHK(hipMemcpyAsync(logits + (size_t)r * BT, h->tc_logits + (size_t)r * BT, BT * 4,
+                              hipMemcpyDeviceToDevice, s));
+    } else {
+      for (int r = 1; r <= R; ++r)
+        HIPCHK(hipMemcpyAsync(logits + (size_t)(r - 1) * BT, z_r(r), BT * 4, hipMemcpyDeviceToDevice, s));
+    }
+  }
+  return MOR_OK;
+}
+
+template <typename T>
+mor_status copy_block(mor_handle_s* h, const mor_block_weights& src, const BlockPacked& dst,
+                      hipStream_t s) {
+  const mor_config& c = h->cfg;
+  const size_t d = c.d_model, es = sizeof(T);
+  const void* ptrs[] = {src.wq, src.wk, src.wv, src.wo, src.w_gate, src.w_up, src.w_down, src.g_attn, src.g_ffn};
+  for (const void* p : ptrs)
+    if (!p) return fail(MOR_E_INVALID, "null weight pointer");
+  char* q = reinterpret_cast<char*>(dst.wqkv);
+  HIPCHK(hipMemcpyAsync(q, src.wq, h->nq * d * es, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(q + h->nq * d * es, src.wk, h->nkv * d * es, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(q + (h->nq + h->nkv) * d * es, src.wv, h->nkv * d * es, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(dst.wo, src.wo, d * h->nq * es, hipMemcpyDeviceToDevice, s));
+  HIPCHK(launch_pack_gate_up<T>(reinterpret_cast<const T*>(src.w_gate), reinterpret_cast<const T*>(src.w_up),
+                                reinterpret_cast<T*>(dst.wgu), c.d_ff, c.d_model, s));
+  HIPCHK(hipMemcpyAsync(dst.wd, src.w_down, d * c.d_ff * es, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(dst.g_attn, src.g_attn, d * 4, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(dst.g_ffn, src.g_ffn, d * 4, hipMemcpyDeviceToDevice, s));
+  return MOR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mor_abi_version(void) { return MOR_ABI_VERSION; }
+
+const char* mor_last_error(void) { return g_err.c_str(); }
+
+size_t mor_workspace_bytes(const mor_config* cfg) {
+  if (validate(cfg) != MOR_OK) return 0;
+  return plan(*cfg, nullptr, nullptr);
+}
+
+mor_status mor_init(const mor_config* cfg, const mor_weights* w, void* workspace,
+                    size_t workspace_bytes, void* stream, mor_handle** out) {
+  mor_status st = validate(cfg);
+  if (st != MOR_OK) return st;
+  if (!w || !workspace || !out) return fail(MOR_E_INVALID, "null weights, workspace or out");
+  if (!w->router_w) return fail(MOR_E_INVALID, "null router_w");
+  const int n_s = (cfg->n_layers - 2) / cfg->n_rec;
+  if (!w->shared) return fail(MOR_E_INVALID, "null shared weights");
+  const size_t need = plan(*cfg, nullptr, nullptr);
+  if (workspace_bytes < need)
+    return fail(MOR_E_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " + std::to_string(need));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto* h = new mor_handle_s();
+  h->cfg = *cfg;
+  char* base = reinterpret_cast<char*>(((uintptr_t)workspace + kAlign - 1) / kAlign * kAlign);
+  plan(*cfg, h, base);
+  auto cleanup = [&](mor_status e) { delete h; return e; };
+  for (int i = 0; i < n_s + 2; ++i) {
+    const mor_block_weights& src = i == 0 ? w->first : i == n_s + 1 ? w->last : w->shared[i - 1];
+    st = cfg->dtype == MOR_BF16 ? copy_block<bf16>(h, src, h->blk[i], s) : copy_block<float>(h, src, h->blk[i], s);
+    if (st != MOR_OK) return cleanup(st);
+  }
+  const size_t d = cfg->d_model, R = cfg->n_rec;
+  hipError_t e = hipMemcpyAsync(h->router_w, w->router_w, R * d * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) {
+    h->has_bias = w->router_b != nullptr;
+    e = h->has_bias ? hipMemcpyAsync(h->router_b, w->router_b, R * 4, hipMemcpyDeviceToDevice, s)
+                    : hipMemsetAsync(h->router_b, 0, R * 4, s);
+  }
+  // RoPE table: angle pos * theta^(-2i/hd), evaluated in double, stored fp32.
+  const int half = cfg->head_dim / 2;
+  std::vector<float> cs((size_t)cfg->max_seq * half), sn((size_t)cfg->max_seq * half);
+  for (int p = 0; p < cfg->max_seq; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double inv = std::pow((double)cfg->rope_theta, -(2.0 * i) / cfg->head_dim);
+      const double a = p * inv;
+      cs[(size_t)p * half + i] = (float)std::cos(a);
+      sn[(size_t)p * half + i] = (float)std::sin(a);
+    }
+  if (e == hipSuccess) e = hipMemcpyAsync(h->rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(h->rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemsetAsync(h->err, 0, 64, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    delete h;
+    return fail(MOR_E_HIP, std::string("mor_init: ") + hipGetErrorString(e));
+  }
+  *out = h;
+  return MOR_OK;
+}
+
+mor_status mor_prefill(mor_handle* h, const float* h_in, int32_t B, int32_t T, float* h_out,
+                       int32_t* sel_pos, int32_t* counts, float* logits, float* h_per_rec,
+                       void* stream) {
+  if (!h || !h_in || !h_out) return fail(MOR_E_INVALID, "null handle or hidden-state pointer");
+  if (B < 1 || B > h->cfg.max_batch || T < 1 || T > h->cfg.max_seq)
+    return fail(MOR_E_SHAPE, "B or T outside 1..max_batch / 1..max_seq");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (h->cfg.dtype == MOR_BF16)
+    return prefill_impl<bf16>(h, h_in, B, T, h_out, sel_pos, counts, logits, h_per_rec, s);
+  return prefill_impl<float>(h, h_in, B, T, h_out, sel_pos, counts, logits, h_per_rec, s);
+}
+
+mor_status mor_route(mor_handle* h, const float* H, const int32_t* active_in,
+                     const int32_t* counts_in, int32_t r, int32_t B, int32_t T,
+                     int32_t* active_out, int32_t* counts_out, float* z_out, void* stream) {
+  if (!h || !H || !active_in || !counts_in || !active_out || !counts_out || !z_out)
+    return fail(MOR_E_INVALID, "null pointer");
+  const mor_config& c = h->cfg;
+  if (c.routing == MOR_ROUTE_TOKEN_CHOICE) return fail(MOR_E_STATE, "mor_route: token choice not supported");
+  if (r < 1 || r > c.n_rec) return fail(MOR_E_INVALID, "r outside 1..n_rec");
+  if (B < 1 || B > c.max_batch || T < 1 || T > c.max_seq) return fail(MOR_E_SHAPE, "B or T out of range");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t MT = h->MT, BT = (size_t)B * T;
+  int* meta_s = h->meta + (size_t)(c.n_rec + 1) * (c.max_batch + 1);
+  HIPCHK(launch_fill_f32(z_out, BT, NAN, s));
+  HIPCHK(launch_offsets(counts_in, B, meta_s, s));
+  HIPCHK(launch_gather(H, c.d_model, active_in, meta_s, B, T, (int)BT, GATE_ASSIGN, nullptr, nullptr,
+                       nullptr, r, h->X, h->rows, h->rows + MT, h->rows + 2 * MT, h->rows + 3 * MT,
+                       h->gate, s));
+  HIPCHK(launch_router(H, c.d_model, h->rows + MT, meta_s, (int)BT, h->router_w + (size_t)(r - 1) * c.d_model,
+                       h->has_bias ? h->router_b + (r - 1) : nullptr, z_out, s));
+  const int k = ceil_div((long)c.cap_num[r - 1] * T, c.cap_den);
+  const int mode = c.routing == MOR_ROUTE_EC_TOPK ? SEL_EC : SEL_THRESHOLD;
+  HIPCHK(launch_select(mode, B, T, z_out, nullptr, active_in, counts_in, k, r, active_out, counts_out, h->err, s));
+  return MOR_OK;
+}
+
+mor_status mor_kv_view(mor_handle* h, int32_t stream, const void** k, const void** v_t,
+                       int32_t* kpad) {
+  if (!h || !k || !v_t || !kpad) return fail(MOR_E_INVALID, "null pointer");
+  if (stream < 0 || stream >= h->nstreams) return fail(MOR_E_INVALID, "stream index out of range");
+  *k = kv_k(h, stream);
+  *v_t = kv_vt(h, stream);
+  *kpad = h->kpad;
+  return MOR_OK;
+}
+
+mor_status mor_get_error_flags(mor_handle* h, void* stream, uint32_t* flags) {
+  if (!h || !flags) return fail(MOR_E_INVALID, "null pointer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  HIPCHK(hipMemcpyAsync(flags, h->err, 4, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  HIPCHK(hipMemsetAsync(h->err, 0, 4, s));
+  HIPCHK(hipStreamSynchronize(s));
+  return MOR_OK;
+}
+
+void mor_destroy(mor_handle* h) { delete h; }
+
+}  // extern "C"

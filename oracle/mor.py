@@ -280,6 +280,11 @@ def _prefill_one(cfg, W, h0, ks, forced, gate_mode, update):
         depth = np.argmax(Z, axis=1) + 1            # argmax returns the lowest index on ties
         probs = _softmax(Z.astype(np.float64))
         z_list = [Z]
+        own_depth = depth.copy()
+        if forced is not None:                      # teacher forcing: depth = last set holding t
+            depth = np.zeros(T, np.int64)
+            for r in range(1, R + 1):
+                depth[np.asarray(forced[r - 1], np.int64)] = r
     for r in range(1, R + 1):
         if cfg.routing == "ec":
             z = router_logits_fp32(H[active], W["router_w"][r - 1])
@@ -291,14 +296,15 @@ def _prefill_one(cfg, W, h0, ks, forced, gate_mode, update):
         elif cfg.routing == "threshold":
             z = router_logits_fp32(H[active], W["router_w"][r - 1], W["router_b"][r - 1])
             keep = np.ones(len(active), bool) if r == 1 else (z > 0)
-            sel = active[keep]
-            g = sigmoid(z[keep])
+            own = active[keep]
+            sel = own if forced is None else np.asarray(forced[r - 1])
+            g = sigmoid(z[np.searchsorted(active, sel)])
             z_list.append((active.copy(), z))
-            own_list.append(sel)
+            own_list.append(own)
         elif cfg.routing == "tc":
+            own_list.append(pos_all[own_depth >= r])
             sel = pos_all[depth >= r]
             g = np.where(depth[sel] == r, probs[sel, r - 1], 1.0)
-            own_list.append(sel)
         else:
             raise ValueError(cfg.routing)
         X = H[sel]
@@ -337,6 +343,7 @@ def _prefill_one(cfg, W, h0, ks, forced, gate_mode, update):
            "hist": hist, "kv": kv}
     if cfg.routing == "tc":
         res["depth"] = depth
+        res["own_depth"] = own_depth
     return res
 
 
@@ -351,7 +358,8 @@ def prefill(cfg, weights, H0: np.ndarray, forced_sel=None, gate_mode: Optional[s
     (recursive KV sharing, [Notes] 3.2), and merges the result with the gate.
 
     forced_sel: optional [N_r][B] position arrays to use instead of the oracle's own
-    top-k (teacher forcing); the oracle's own choice is still returned in "own_sel".
+    selection (teacher forcing, any routing mode); the oracle's own choice is still
+    returned in "own_sel" ("own_depth" for token choice).
     Returns a dict of per-sequence lists plus "out" [B, T, d].
     """
     W = to_f64_weights(weights)

@@ -1,0 +1,207 @@
+"""GPU parity of the HIP library against the CPU oracle (needs an MI355X).
+
+Bars (BASELINE the benchmark spec): routing bit-exact (selected positions, counts, and the fp32 router
+logits given the same H); hidden states within max relative error 1e-4 (fp32 configs) and
+2e-2 (bf16 configs), per token row as max|diff| / max|ref|.
+fp32 configs run free (the oracle makes its own routing decisions and must agree). bf16
+configs are teacher-forced for the hidden-state comparison: the oracle adopts the GPU's
+active sets, after the stage-wise check has shown that each set is exactly what the oracle
+selects from the GPU's own H^r.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workload
+from tests.gpu_common import (build_gpu, check_routing_stagewise, gpu_sets, rel_err, run_prefill,
+                              say, tolerance)
+
+pytestmark = pytest.mark.gpu
+
+
+def _compare_prefill(cfg, weights=None, forced=None, batch_subset=None):
+    model, W = build_gpu(cfg, weights)
+    H0 = workload.make_inputs(cfg)
+    res = run_prefill(model, H0)
+    check_routing_stagewise(cfg, W, res, H0)
+    B = H0.shape[0]
+    seqs = range(B) if batch_subset is None else batch_subset
+    teacher = cfg.dtype == "bf16" if forced is None else forced
+    worst = 0.0
+    for b in seqs:
+        sets = gpu_sets(res, cfg, b)
+        fs = [[s] for s in sets] if teacher else None
+        ref = oracle.prefill(cfg, W, H0[b:b + 1], forced_sel=fs)
+        p = ref["per_seq"][0]
+        if not teacher:
+            for r in range(cfg.n_rec):
+                assert np.array_equal(p["sel"][r], sets[r]), f"free-running routing differs r={r + 1} seq {b}"
+        for r in range(cfg.n_rec + 1):
+            e = rel_err(res["h_per_rec"][r, b], p["hist"][r])
+            assert e <= tolerance(cfg), f"H after stage {r} seq {b}: rel err {e}"
+        e = rel_err(res["out"][b], ref["out"][0])
+        worst = max(worst, e)
+        assert e <= tolerance(cfg), f"output seq {b}: rel err {e}"
+    say(f"[gpu] {cfg.name}: worst output rel err {worst:.3e}")
+    model.close()
+    return res
+
+
+def test_tiny_f32_free_running():
+    _compare_prefill(workload.get_config("tiny_f32"))
+
+
+def test_small_f32_ragged_free_running():
+    _compare_prefill(workload.get_config("small_f32"))
+
+
+def test_small_f32_unit_gate_full_capacity():
+    """Capacity 1 everywhere with unit gating: the fixed-depth recursive model."""
+    _compare_prefill(workload.get_config("small_f32", gate_mode="unit", cap_num=(3, 3, 3)))
+
+
+def test_small_bf16_teacher_forced():
+    _compare_prefill(workload.get_config("small_bf16"))
+
+
+def test_small_bf16_kv_share():
+    _compare_prefill(workload.get_config("small_share_bf16"))
+
+
+def test_small_bf16_token_choice():
+    _compare_prefill(workload.get_config("small_tc_bf16"))
+
+
+def test_small_f32_token_choice_free_running():
+    _compare_prefill(workload.get_config("small_tc_bf16", dtype="f32"))
+
+
+def test_small_f32_kv_share_free_running():
+    _compare_prefill(workload.get_config("small_share_bf16", dtype="f32"))
+
+
+def test_small_threshold_bf16():
+    cfg = workload.get_config("small_thr_bf16")
+    W = workload.make_weights(cfg)
+    W["router_b"] = np.array([0.0, 0.1, 0.0, -0.1], np.float32)
+    _compare_prefill(cfg, weights=W)
+
+
+def test_single_token_and_single_sequence():
+    """Degenerate shapes: T = 1 (every capacity keeps the one token) and B = 1."""
+    cfg = workload.get_config("small_f32", batch=1, seq=1)
+    _compare_prefill(cfg)
+    _compare_prefill(workload.get_config("small_bf16", batch=1, seq=65))
+
+
+def test_kv_cache_contents():
+    """The per-recursion caches hold exactly the oracle's K (RoPE'd) and V of the active tokens."""
+    import torch
+    cfg = workload.get_config("small_bf16", batch=2, seq=150)
+    model, W = build_gpu(cfg)
+    H0 = workload.make_inputs(cfg)
+    res = run_prefill(model, H0)
+    n_s = cfg.n_shared
+    for b in range(cfg.batch):
+        sets = gpu_sets(res, cfg, b)
+        ref = oracle.prefill(cfg, W, H0[b:b + 1], forced_sel=[[s] for s in sets], keep_kv=True)
+        kv = ref["per_seq"][0]["kv"]
+        streams = {0: kv["first"], 1 + cfg.n_rec * n_s: kv["last"]}
+        for r in range(1, cfg.n_rec + 1):
+            for j in range(1, n_s + 1):
+                streams[1 + (r - 1) * n_s + (j - 1)] = kv[(r, j)]
+        for sid, (k_ref, v_ref, pos) in streams.items():
+            kt, vt = model.kv_tensors(sid, cfg.batch)
+            n = len(pos)
+            k_gpu = kt[b, :n].float().cpu().numpy()
+            v_gpu = vt[b].float().cpu().numpy().transpose(2, 0, 1)[:n]
+            assert rel_err(k_gpu, k_ref) < 2e-2 and rel_err(v_gpu, v_ref) < 2e-2, f"stream {sid}"
+    model.close()
+
+
+def test_determinism_bitwise():
+    import torch
+    cfg = workload.get_config("small_bf16")
+    model, W = build_gpu(cfg)
+    H0 = workload.make_inputs(cfg)
+    a = run_prefill(model, H0)
+    b = run_prefill(model, H0)
+    for k in ("out", "sel_pos", "counts", "logits", "h_per_rec"):
+        assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
+    model.close()
+
+
+def test_route_entry_bit_exact_with_ties_and_nan():
+    """mor_route on crafted inputs: duplicated rows force exactly tied logits (lower position
+    wins), a NaN row ranks last and raises the error flag, -0 logits count as +0."""
+    import torch
+    cfg = workload.get_config("small_f32", batch=2, seq=97)
+    model, W = build_gpu(cfg)
+    rng = np.random.default_rng(7)
+    B, T, d = 2, 97, cfg.d_model
+    H = rng.standard_normal((B, T, d)).astype(np.float32)
+    H[0, 10] = H[0, 50] = H[0, 70]           # identical logits
+    H[1, 5] = H[1, 6]
+    H[1, 40] = 0.0                           # logit exactly 0
+    H[1, 90] = np.nan
+    act = np.full((B, T), -1, np.int32)
+    cnt = np.zeros(B, np.int32)
+    prev = [np.arange(T), np.sort(rng.choice(T, 60, replace=False))]
+    prev[1] = np.union1d(prev[1], [5, 6, 40, 90]).astype(np.int32)
+    for b in range(B):
+        act[b, :len(prev[b])] = prev[b]
+        cnt[b] = len(prev[b])
+    Hd = torch.from_numpy(H).cuda()
+    for r in (1, 2, 3):
+        say(f"[gpu] mor_route r={r}")
+        a_out, c_out, z = model.route(Hd, torch.from_numpy(act).cuda(), torch.from_numpy(cnt).cuda(), r)
+        a_out, c_out, z = a_out.cpu().numpy(), c_out.cpu().numpy(), z.cpu().numpy()
+        k = oracle.capacity_counts(cfg.cap_num, cfg.cap_den, T)[r - 1]
+        for b in range(B):
+            zr = oracle.router_logits_fp32(H[b][prev[b]], W["router_w"][r - 1])
+            zg = z[b][prev[b]]
+            same = (zg.view(np.uint32) == zr.view(np.uint32)) | (np.isnan(zg) & np.isnan(zr))
+            assert same.all()
+            finite = ~np.isnan(zr)
+            order = np.lexsort((prev[b][finite], -zr[finite].astype(np.float64)))
+            ranked = list(prev[b][finite][order]) + list(prev[b][~finite])
+            want = np.sort(np.array(ranked[:min(k, len(ranked))]))
+            assert c_out[b] == len(want)
+            assert np.array_equal(a_out[b, :c_out[b]], want)
+    assert model.error_flags() & 1
+    assert model.error_flags() == 0          # cleared by the read
+    model.close()
+
+
+def test_invalid_shapes_rejected():
+    import torch
+    import adaptive_depth_recursive_amd as mor
+    cfg = workload.get_config("tiny_f32")
+    model, _ = build_gpu(cfg)
+    h = torch.zeros((cfg.batch + 1, cfg.seq, cfg.d_model), device="cuda")
+    with pytest.raises(mor.MorError) as e:
+        model.prefill(h)
+    assert e.value.status == mor.MOR_E_SHAPE
+    model.close()
+
+
+@pytest.mark.parametrize("name", ["smol360m_bf16", "smol135m_bf16"])
+def test_full_size_sampled(name):
+    """Full-size prefill (8 x 2048), the launch configuration the benchmark times: routing is
+    checked stage-wise and bit-exactly for every sequence; hidden states on one sequence,
+    teacher-forced, against the oracle."""
+    cfg = workload.get_config(name)
+    model, W = build_gpu(cfg)
+    H0 = workload.make_inputs(cfg)
+    res = run_prefill(model, H0)
+    check_routing_stagewise(cfg, W, res, H0)
+    ks = oracle.capacity_counts(cfg.cap_num, cfg.cap_den, cfg.seq)
+    assert np.array_equal(res["counts"], np.repeat(np.array(ks)[:, None], cfg.batch, axis=1))
+    b = 5
+    sets = gpu_sets(res, cfg, b)
+    say(f"[cpu] oracle on sequence {b} of {name}")
+    ref = oracle.prefill(cfg, W, H0[b:b + 1], forced_sel=[[s] for s in sets])
+    e = rel_err(res["out"][b], ref["out"][0])
+    say(f"[gpu] {name}: seq {b} output rel err {e:.3e}")
+    assert e <= 2e-2
+    model.close()
