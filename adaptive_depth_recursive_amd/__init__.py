@@ -81,6 +81,10 @@ def lib() -> ctypes.CDLL:
                                   ctypes.POINTER(i32)]
         L.mor_get_error_flags.restype = i32
         L.mor_get_error_flags.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
+        L.mor_timing_enable.restype = i32
+        L.mor_timing_enable.argtypes = [vp, i32, i32]
+        L.mor_timing_read.restype = i32
+        L.mor_timing_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
         L.mor_destroy.restype = None
         L.mor_destroy.argtypes = [vp]
         _lib = L
@@ -88,7 +92,9 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("mor_abi_version", "mor_last_error", "mor_workspace_bytes", "mor_init",
-            "mor_prefill", "mor_route", "mor_kv_view", "mor_get_error_flags", "mor_destroy")
+            "mor_prefill", "mor_route", "mor_kv_view", "mor_get_error_flags", "mor_timing_enable",
+            "mor_timing_read", "mor_destroy")
+KERNEL_KINDS = {"qkv": 1, "attention": 2, "o_proj": 3, "gate_up": 4, "down": 5}
 
 
 def _check(status: int):
@@ -251,6 +257,15 @@ class Mor:
         kt = self.workspace[k - base:k - base + n * es].view(dt).view(B, kpad, Hkv, hd)
         vt = self.workspace[v - base:v - base + n * es].view(dt).view(B, Hkv, hd, kpad)
         return kt, vt
+
+    def timing_enable(self, kind: str, max_launches: int):
+        _check(lib().mor_timing_enable(self.handle, KERNEL_KINDS[kind] if kind else 0, max_launches))
+
+    def timing_read(self):
+        """(summed kernel milliseconds, launches) recorded since timing_enable / the last read."""
+        ms, n = ctypes.c_double(), ctypes.c_int32()
+        _check(lib().mor_timing_read(self.handle, ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value
 
     def error_flags(self, stream=None) -> int:
         f = ctypes.c_uint32()

@@ -88,6 +88,11 @@ struct mor_handle_s {
   int* rows = nullptr;           // 4 x [MT]: the same for the current active set
   float* gate = nullptr;         // [MT]
   unsigned* err = nullptr;
+  // measurement: HIP events around every launch of one kernel kind
+  int timing_kind = 0;
+  std::vector<hipEvent_t> ev;
+  size_t ev_used = 0;
+  hipStream_t ev_stream = nullptr;
 };
 
 namespace {
@@ -197,6 +202,28 @@ struct KeySet {
   const int* kcnt;     // [B]
 };
 
+enum { KIND_QKV = 1, KIND_ATTN = 2, KIND_O = 3, KIND_GATE_UP = 4, KIND_DOWN = 5 };
+
+// Brackets one launch with a pair of events when this kind is being timed.
+struct TimedLaunch {
+  mor_handle_s* h;
+  bool on;
+  hipStream_t s;
+  TimedLaunch(mor_handle_s* h_, int kind, hipStream_t s_)
+      : h(h_), on(h_->timing_kind == kind && h_->ev_used + 2 <= h_->ev.size()), s(s_) {
+    if (on) {
+      (void)hipEventRecord(h->ev[h->ev_used], s);
+      h->ev_stream = s;
+    }
+  }
+  ~TimedLaunch() {
+    if (on) {
+      (void)hipEventRecord(h->ev[h->ev_used + 1], s);
+      h->ev_used += 2;
+    }
+  }
+};
+
 template <typename E>
 mor_status run_layer(mor_handle_s* h, const BlockPacked& w, float* X, const RowSet& rs,
                      void* k_dst, void* vt_dst, const KeySet& keys, int B, int T, hipStream_t s) {
@@ -212,7 +239,10 @@ mor_status run_layer(mor_handle_s* h, const BlockPacked& w, float* X, const RowS
   ep.rowpos = rs.rows; ep.rowseq = rs.rows + 2 * (size_t)MT; ep.rowidx = rs.rows + 3 * (size_t)MT;
   ep.rope_cos = h->rope_cos; ep.rope_sin = h->rope_sin;
   const int n_qkv = k_dst ? h->nqkv : h->nq;
-  HIPCHK(launch_gemm<E>(EPI_QKV, Xn, reinterpret_cast<const E*>(w.wqkv), n_qkv, d, rs.m_upper, rs.meta, ep, s));
+  {
+    TimedLaunch t(h, KIND_QKV, s);
+    HIPCHK(launch_gemm<E>(EPI_QKV, Xn, reinterpret_cast<const E*>(w.wqkv), n_qkv, d, rs.m_upper, rs.meta, ep, s));
+  }
 
   AttnArgs aa{};
   aa.q = h->Q; aa.ldq = h->nq; aa.qmeta = rs.meta; aa.qcnt = rs.cnt; aa.qpos = rs.rows;
@@ -220,16 +250,28 @@ mor_status run_layer(mor_handle_s* h, const BlockPacked& w, float* X, const RowS
   aa.kpad = h->kpad; aa.hkv = c.n_kv_heads; aa.hq = c.n_q_heads; aa.hd = c.head_dim;
   aa.o = h->O; aa.ldo = h->nq;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
-  HIPCHK(launch_attention<E>(aa, B, rs.max_per_seq, s));
+  {
+    TimedLaunch t(h, KIND_ATTN, s);
+    HIPCHK(launch_attention<E>(aa, B, rs.max_per_seq, s));
+  }
 
   GemmEpi er{};
   er.x = X; er.ldx = d;
-  HIPCHK(launch_gemm<E>(EPI_RESID, reinterpret_cast<const E*>(h->O), reinterpret_cast<const E*>(w.wo), d, h->nq, rs.m_upper, rs.meta, er, s));
+  {
+    TimedLaunch t(h, KIND_O, s);
+    HIPCHK(launch_gemm<E>(EPI_RESID, reinterpret_cast<const E*>(h->O), reinterpret_cast<const E*>(w.wo), d, h->nq, rs.m_upper, rs.meta, er, s));
+  }
   HIPCHK(launch_rmsnorm<E>(X, d, rs.meta, rs.m_upper, w.g_ffn, c.rms_eps, Xn, s));
   GemmEpi eg{};
   eg.h = h->Hf; eg.ldh = dff;
-  HIPCHK(launch_gemm<E>(EPI_SWIGLU, Xn, reinterpret_cast<const E*>(w.wgu), 2 * dff, d, rs.m_upper, rs.meta, eg, s));
-  HIPCHK(launch_gemm<E>(EPI_RESID, reinterpret_cast<const E*>(h->Hf), reinterpret_cast<const E*>(w.wd), d, dff, rs.m_upper, rs.meta, er, s));
+  {
+    TimedLaunch t(h, KIND_GATE_UP, s);
+    HIPCHK(launch_gemm<E>(EPI_SWIGLU, Xn, reinterpret_cast<const E*>(w.wgu), 2 * dff, d, rs.m_upper, rs.meta, eg, s));
+  }
+  {
+    TimedLaunch t(h, KIND_DOWN, s);
+    HIPCHK(launch_gemm<E>(EPI_RESID, reinterpret_cast<const E*>(h->Hf), reinterpret_cast<const E*>(w.wd), d, dff, rs.m_upper, rs.meta, er, s));
+  }
   return MOR_OK;
 }
 
@@ -470,6 +512,38 @@ mor_status mor_get_error_flags(mor_handle* h, void* stream, uint32_t* flags) {
   return MOR_OK;
 }
 
-void mor_destroy(mor_handle* h) { delete h; }
+mor_status mor_timing_enable(mor_handle* h, int32_t kind, int32_t max_launches) {
+  if (!h) return fail(MOR_E_INVALID, "null handle");
+  if (kind < 0 || kind > KIND_DOWN || max_launches < 0) return fail(MOR_E_INVALID, "kind or max_launches");
+  for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
+  h->ev.clear();
+  h->ev_used = 0;
+  h->timing_kind = kind;
+  if (kind == 0) return MOR_OK;
+  h->ev.resize(2 * (size_t)max_launches, nullptr);
+  for (auto& e : h->ev) HIPCHK(hipEventCreate(&e));
+  return MOR_OK;
+}
+
+mor_status mor_timing_read(mor_handle* h, double* total_ms, int32_t* launches) {
+  if (!h || !total_ms || !launches) return fail(MOR_E_INVALID, "null pointer");
+  double acc = 0.0;
+  if (h->ev_used) HIPCHK(hipEventSynchronize(h->ev[h->ev_used - 1]));
+  for (size_t i = 0; i + 1 < h->ev_used; i += 2) {
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, h->ev[i], h->ev[i + 1]));
+    acc += ms;
+  }
+  *total_ms = acc;
+  *launches = (int32_t)(h->ev_used / 2);
+  h->ev_used = 0;
+  return MOR_OK;
+}
+
+void mor_destroy(mor_handle* h) {
+  if (!h) return;
+  for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
+  delete h;
+}
 
 }  // extern "C"

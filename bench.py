@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoR prefill on one MI355X (the 360M-shape, N_r = 3, bf16 workload).
+
+One step = one mor_prefill call over a batch of 8 sequences of 2048 tokens: first layer,
+three expert-choice recursions (capacities 3/3, 2/3, 1/3) over 10 shared layers with
+recursion-wise KV caching, last layer. Inputs and weights are seeded synthetic tensors already
+resident in HBM when the timed region starts.
+
+Prints one JSON line. Algorithmic FLOPs follow the MoR paper's Appendix D accounting: 2 x
+parameters per token for the projections, attention QK^T and PV counted over the causal
+triangle only, norms and nonlinearities excluded, each recursion counted over the tokens
+actually active there.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15          # dense MFMA bf16, FLOP/s (MI355X)
+PEAK_FP32 = 157.3e12
+PEAK_HBM = 8.0e12           # B/s
+KERNEL_SOURCES = {"gate_up": "adaptive_depth_recursive_amd/csrc/k_gemm.hip",
+                  "qkv": "adaptive_depth_recursive_amd/csrc/k_gemm.hip",
+                  "o_proj": "adaptive_depth_recursive_amd/csrc/k_gemm.hip",
+                  "down": "adaptive_depth_recursive_amd/csrc/k_gemm.hip",
+                  "attention": "adaptive_depth_recursive_amd/csrc/k_attn.hip"}
+
+
+def layer_params(cfg) -> int:
+    d, hd = cfg.d_model, cfg.head_dim
+    nq, nkv = cfg.n_q_heads * hd, cfg.n_kv_heads * hd
+    return d * (nq + 2 * nkv) + nq * d + 2 * d * cfg.d_ff + cfg.d_ff * d
+
+
+def flop_counts(cfg, counts, sel_pos=None):
+    """Algorithmic FLOPs of one call from the realised active-set sizes counts[r][b]."""
+    import numpy as np
+    B, T, R, n_s = counts.shape[1], cfg.seq, cfg.n_rec, cfg.n_shared
+    d, hd, Hq = cfg.d_model, cfg.head_dim, cfg.n_q_heads
+    P = layer_params(cfg)
+    P_q_only = P - 2 * d * cfg.n_kv_heads * hd
+    tri = lambda n: n * (n + 1) // 2          # causal (query, key) pairs of n tokens
+    linear = 2 * P * 2 * B * T
+    attn = 2 * 4 * Hq * hd * B * tri(T)
+    gate_up = 2 * d * 2 * cfg.d_ff * 2 * B * T
+    for r in range(R):
+        M = int(counts[r].sum())
+        share = cfg.kv_mode == "share" and r >= 1
+        linear += n_s * 2 * (P_q_only if share else P) * M
+        gate_up += n_s * 2 * d * 2 * cfg.d_ff * M
+        if share:
+            pairs = 0
+            for b in range(B):
+                pos = sel_pos[r, b, :counts[r, b]]
+                k1 = sel_pos[0, b, :counts[0, b]]
+                pairs += int(np.searchsorted(k1, pos, side="right").sum())
+            attn += n_s * 4 * Hq * hd * pairs
+        else:
+            attn += n_s * 4 * Hq * hd * sum(tri(int(c)) for c in counts[r])
+    if cfg.routing == "tc":
+        router = 2 * d * R * B * T
+    else:
+        router = 2 * d * (B * T + sum(int(counts[r].sum()) for r in range(R - 1)))
+    return {"linear": linear, "attention": attn, "router": router,
+            "total": linear + attn + router, "gate_up": gate_up,
+            "gate_up_launches": 2 + R * n_s}
+
+
+def source_hash(path: str) -> str:
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel: str, workload_name: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the current
+    kernel source (null otherwise)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_gemm_{workload_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, weights, H0_np, seq_len: int):
+    """The oracle, as it stands, on one sequence of the same workload (host cores)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    x = np.ascontiguousarray(H0_np[:1, :seq_len])
+    t0 = time.perf_counter()
+    oracle.prefill(cfg.replace(seq=seq_len), weights, x)
+    dt = time.perf_counter() - t0
+    return {"value": seq_len / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 of {cfg.batch} sequences ({seq_len} tokens) of the same prefill, "
+                      f"oracle in float64 with bf16 storage points; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="smol360m_bf16")
+    ap.add_argument("--roofline-kernel", default="gate_up", choices=sorted(KERNEL_SOURCES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seq", type=int, default=2048, help="tokens of the CPU-baseline sample")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the MoR prefill shards by sequence with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import adaptive_depth_recursive_amd as mor
+    import workload
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4}))
+        return
+
+    cfg = workload.get_config(args.config)
+    W = workload.make_weights(cfg)
+    H0 = workload.make_inputs(cfg)
+    model = mor.Mor(cfg, W)
+    h = torch.from_numpy(H0).cuda()
+    h_out = torch.empty_like(h)
+    B, T = cfg.batch, cfg.seq
+
+    # realised active sets (static counts for expert choice) for the FLOP accounting
+    outs = model.prefill_outputs(h, debug=False)
+    torch.cuda.synchronize()
+    counts = outs["counts"].cpu().numpy()
+    sel_pos = outs["sel_pos"].cpu().numpy()
+    del outs
+    fl = flop_counts(cfg, counts, sel_pos)
+
+    for _ in range(args.warmup):
+        model.prefill(h, h_out)
+    torch.cuda.synchronize()
+
+    kind = args.roofline_kernel
+    launches_per_call = fl["gate_up_launches"]
+    model.timing_enable(kind, launches_per_call * args.steps)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        model.prefill(h, h_out)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = start.elapsed_time(end)
+    k_ms, k_n = model.timing_read()
+    model.timing_enable("", 0)
+
+    step_s = ms / 1e3 / args.steps
+    tokens_per_s = B * T / step_s
+    if kind == "gate_up":
+        k_flops_per_launch = fl["gate_up"] / launches_per_call
+    else:
+        k_flops_per_launch = None
+    k_avg_s = (k_ms / 1e3) / max(k_n, 1)
+    peak = PEAK_BF16 if cfg.dtype == "bf16" else PEAK_FP32
+    achieved = k_flops_per_launch / k_avg_s / 1e12 if k_flops_per_launch else None
+    traffic = traffic_from_profile(kind, cfg.name)
+    roofline = {"bound": "mfma", "kernel": f"k_gemm<bf16,128,128,SWIGLU> ({kind} projection)",
+                "achieved": achieved, "peak": peak / 1e12, "unit": "TFLOP/s",
+                "frac": (achieved * 1e12 / peak) if achieved else None, "traffic": traffic,
+                "avg_launch_us": k_avg_s * 1e6, "launches_timed": k_n,
+                "flops_per_launch": k_flops_per_launch}
+
+    result = {
+        "metric": "MoR prefill tokens/sec (360M-shape, N_r=3, bf16) + % of bf16 MFMA peak",
+        "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": step_s * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name} prefill: batch {B} x seq {T}, d {cfg.d_model}, "
+                               f"{cfg.n_q_heads}/{cfg.n_kv_heads} heads x {cfg.head_dim}, FFN {cfg.d_ff}, "
+                               f"L {cfg.n_layers} (N_r {cfg.n_rec} x {cfg.n_shared} shared), "
+                               f"EC capacities {'/'.join(str(c) for c in cfg.cap_num)} of {cfg.cap_den}, "
+                               f"{cfg.kv_mode}-wise KV",
+                   "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
+        "step_flops": fl["total"],
+        "step_mfma_frac": fl["total"] / step_s / peak,
+        "wall_s_timed": wall,
+        "roofline": roofline,
+    }
+    model.close()
+    del h, h_out
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, W, H0, args.cpu_seq)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

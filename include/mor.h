@@ -157,6 +157,15 @@ mor_status mor_kv_view(mor_handle* h, int32_t stream, const void** k, const void
 /* Reads and clears the device error flags (bit 0: a NaN router logit). Synchronises `stream`. */
 mor_status mor_get_error_flags(mor_handle* h, void* stream, uint32_t* flags);
 
+/* Measurement hooks. mor_timing_enable makes later calls record a pair of HIP events, on the
+ * call's stream, around every launch of one kernel kind: 1 QKV projection, 2 attention,
+ * 3 output projection, 4 gate/up projection (SwiGLU), 5 down projection; 0 turns it off.
+ * At most max_launches launches are recorded (events are created here, not during calls).
+ * mor_timing_read waits for the last recorded event, returns the summed kernel time in ms and
+ * the number of recorded launches, and clears the record. */
+mor_status mor_timing_enable(mor_handle* h, int32_t kind, int32_t max_launches);
+mor_status mor_timing_read(mor_handle* h, double* total_ms, int32_t* launches);
+
 /* Frees the host-side handle. The workspace stays the caller's. NULL is ignored. */
 void mor_destroy(mor_handle* h);
 
