@@ -214,7 +214,7 @@ hipError_t launch_attention(const AttnArgs& a, int B, int max_rows_per_seq, hipS
   dim3 grid((max_rows_per_seq + 63) / 64, B, a.hkv);
   if (grid.x == 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
-    if (a.hd == 64) return launch_hd<T, 64>(a, grid, s);
+    if (a.hd == 64) return launch_attention_bf16(a, grid, s);
   } else {
     if (a.hd == 16) return launch_hd<T, 16>(a, grid, s);
     if (a.hd == 32) return launch_hd<T, 32>(a, grid, s);

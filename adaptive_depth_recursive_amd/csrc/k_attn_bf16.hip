@@ -1,0 +1,234 @@
+// bf16 causal attention over per-recursion active sets (head_dim 64), tuned for gfx950.
+//
+// Same computation as the generic kernel in k_attn.hip (key s visible to query t iff
+// kpos[s] <= qpos[t]; S^T = K Q^T on MFMA, online softmax per query column, P^T fed to the PV
+// product as the B operand, V^T as the A operand), organised for throughput:
+//  - K and V^T tiles of 64 keys stream global -> LDS with global_load_lds_dwordx4 into two
+//    stages, so the next tile is in flight while this one is used;
+//  - the K tile rows are read in a permuted key order, chosen so that the 8 keys a lane holds
+//    for one PV step are 8 consecutive keys: the matching V^T operand is then one 16-byte LDS
+//    read, and the S^T accumulators need no shuffles to become the P^T operand;
+//  - K and V fragments are read once per tile and reused by all query heads of the KV head;
+//  - the running maximum is only raised (and O rescaled) when it grows by more than 2^8, so the
+//    rescale is skipped on most tiles; probabilities are then bounded by 2^8, exact in fp32.
+#include <climits>
+
+#include "mor_internal.h"
+
+namespace mor {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kRow = 128;                          // LDS row: 64 bf16
+
+// V^T tile rows (head-dim index) are read 16 consecutive at a time: swizzle by (row >> 1) & 7.
+__device__ __forceinline__ int swz_v(int row) { return (row >> 1) & 7; }
+// K tile rows are read in the order perm(16h + 4a + b) = 8a + 4h + b within each 32 rows (see
+// kslot); this swizzle gives those 16 rows 16 distinct bank groups.
+__device__ __forceinline__ int swz_k(int row) { return (((row >> 3) & 3) << 1) | ((row >> 1) & 1); }
+
+// LDS row of the K tile read by A-operand row `r` (0..63) of the S^T product.
+__device__ __forceinline__ int kslot(int r) {
+  const int blk = r & ~31, w = r & 31;
+  const int h = w >> 4, a = (w >> 2) & 3, b = w & 3;
+  return blk + 8 * a + 4 * h + b;
+}
+
+template <int ROWS>
+__device__ __forceinline__ void dma_rows(const bf16* src, size_t ld, char* dst, int wave, int lane,
+                                         bool kswz) {
+  constexpr int INSTR = ROWS / 8 / 4;
+#pragma unroll
+  for (int i = 0; i < INSTR; ++i) {
+    const int rb = (i * 4 + wave) * 8;
+    const int r = rb + (lane >> 3);
+    const int c = (lane & 7) ^ (kswz ? swz_k(r) : swz_v(r));
+    __builtin_amdgcn_global_load_lds(src + (size_t)r * ld + c * 8, (lds_void*)(dst + rb * kRow), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ bf16x8 rd(const char* base, int row, int chunk, int sw) {
+  return *reinterpret_cast<const bf16x8*>(base + row * kRow + ((chunk ^ sw) << 4));
+}
+
+}  // namespace
+
+template <int G>
+__global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
+  constexpr int BQ = 64, BKV = 64, HD = 64;
+  constexpr int TILE = 2 * BKV * kRow;               // K tile + V^T tile
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE];
+  __shared__ int sKp[2][BKV];
+
+  const int b = blockIdx.y, kvh = blockIdx.z;
+  const int qb = gridDim.x - 1 - blockIdx.x;         // longest blocks first
+  const int nq = a.qcnt[b];
+  if (qb * BQ >= nq) return;
+  const int nk = a.kcnt[b];
+  const int off = a.qmeta[1 + b];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, g = lane >> 4;
+
+  const int qi = qb * BQ + wave * 16 + fr;
+  const bool qvalid = qi < nq;
+  const int myqpos = qvalid ? a.qpos[off + qi] : INT_MAX;
+  const int wq0 = qb * BQ + wave * 16;
+  const int wave_minpos = wq0 < nq ? a.qpos[off + wq0] : INT_MAX;
+  const int maxpos = a.qpos[off + min(qb * BQ + BQ - 1, nq - 1)];
+  const int* kp = a.kpos + (size_t)b * a.ldkpos;
+  int lo = 0, hi = nk;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (kp[mid] <= maxpos) lo = mid + 1; else hi = mid;
+  }
+  const int kend = lo;
+
+  const bf16* Qb = reinterpret_cast<const bf16*>(a.q);
+  bf16x8 qf[G][2];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      qf[hh][ks] = qvalid ? *reinterpret_cast<const bf16x8*>(Qb + (size_t)(off + qi) * a.ldq + (kvh * G + hh) * HD + ks * 32 + g * 8)
+                          : bf16x8{};
+
+  float mrun[G], lrun[G];
+  f32x4 o[G][4];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    mrun[hh] = -INFINITY;
+    lrun[hh] = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) o[hh][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const size_t ldk = (size_t)a.hkv * HD;
+  const bf16* Kb = reinterpret_cast<const bf16*>(a.k) + (size_t)b * a.kpad * ldk + kvh * HD;
+  const bf16* Vb = reinterpret_cast<const bf16*>(a.vt) + ((size_t)b * a.hkv + kvh) * HD * a.kpad;
+  auto issue = [&](int t0, int buf) {
+    char* st = smem + buf * TILE;
+    dma_rows<BKV>(Kb + (size_t)t0 * ldk, ldk, st, wave, lane, true);
+    dma_rows<HD>(Vb + t0, a.kpad, st + BKV * kRow, wave, lane, false);
+    if (tid < BKV) sKp[buf][tid] = (t0 + tid < nk) ? kp[t0 + tid] : INT_MAX;
+  };
+
+  const float sl2 = a.scale_log2;
+  const int ntiles = (kend + BKV - 1) / BKV;
+  if (ntiles > 0) issue(0, 0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int t0 = t * BKV, buf = t & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < ntiles) issue(t0 + BKV, buf ^ 1);
+    const char* sk = smem + buf * TILE;
+    const char* sv = sk + BKV * kRow;
+    const int* kps = sKp[buf];
+    const bool need_mask = (t0 + BKV > nk) || (kps[BKV - 1] > wave_minpos);
+
+    bf16x8 kf[4][2], vf[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int row = kslot(kb * 16 + fr);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) kf[kb][ks] = rd(sk, row, ks * 4 + g, swz_k(row));
+    }
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const int row = hb * 16 + fr;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) vf[hb][k2] = rd(sv, row, k2 * 4 + g, swz_v(row));
+    }
+
+    // positions of this lane's 16 keys, for the tiles that need the causal mask
+    int kpv[4][4];
+    if (need_mask) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int4 p0 = *reinterpret_cast<const int4*>(&kps[32 * h2 + 8 * g]);
+        const int4 p1 = *reinterpret_cast<const int4*>(&kps[32 * h2 + 8 * g + 4]);
+        kpv[2 * h2][0] = p0.x; kpv[2 * h2][1] = p0.y; kpv[2 * h2][2] = p0.z; kpv[2 * h2][3] = p0.w;
+        kpv[2 * h2 + 1][0] = p1.x; kpv[2 * h2 + 1][1] = p1.y; kpv[2 * h2 + 1][2] = p1.z; kpv[2 * h2 + 1][3] = p1.w;
+      }
+    }
+
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      f32x4 s[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][ks], qf[hh][ks], s[kb], 0, 0, 0);
+      }
+      // s[kb][e] holds the raw score of key 32 (kb/2) + 8 g + 4 (kb & 1) + e of this tile
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[kb][e] = kpv[kb][e] > myqpos ? -INFINITY : s[kb][e];
+      }
+      float mraw = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+#pragma unroll
+      for (int kb = 1; kb < 4; ++kb)
+        mraw = fmaxf(mraw, fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3])));
+      mraw = fmaxf(mraw, __shfl_xor(mraw, 16));
+      mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+      const float mloc = mraw * sl2;                   // scores enter the exponent scaled by sl2
+      if (__any(mloc > mrun[hh] + 8.f)) {              // raise the reference maximum, rescale
+        const float mnew = fmaxf(mrun[hh], mloc);
+        const float alpha = __builtin_amdgcn_exp2f(mrun[hh] - mnew);
+        lrun[hh] *= alpha;
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) o[hh][hb] *= alpha;
+        mrun[hh] = mnew;
+      }
+      const float nm = -mrun[hh];
+      float lsum = 0.f;
+      bf16x8 pf[2];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][e], sl2, nm));
+          lsum += p;
+          pf[kb >> 1][4 * (kb & 1) + e] = (bf16)p;
+        }
+      lrun[hh] += lsum;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          o[hh][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[hb][k2], pf[k2], o[hh][hb], 0, 0, 0);
+    }
+  }
+
+  if (!qvalid) return;
+  bf16* Ob = reinterpret_cast<bf16*>(a.o) + (size_t)(off + qi) * a.ldo;
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    float l = lrun[hh];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const float inv = 1.f / l;
+    const int h = kvh * G + hh;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+      Vec4<bf16>::store(Ob + h * HD + hb * 16 + 4 * g, o[hh][hb][0] * inv, o[hh][hb][1] * inv,
+                        o[hh][hb][2] * inv, o[hh][hb][3] * inv);
+  }
+}
+
+hipError_t launch_attention_bf16(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.hq / a.hkv) {
+    case 1: hipLaunchKernelGGL((k_attn_bf16<1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_attn_bf16<2>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_attn_bf16<3>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_attn_bf16<4>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mor

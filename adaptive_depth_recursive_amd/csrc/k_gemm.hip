@@ -207,13 +207,11 @@ static hipError_t launch_tile(int epi, const T* A, const T* W, int N, int K, int
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_gemm(int epi, const T* A, const T* W, int N, int K, int m_upper,
-                       const int* meta, const GemmEpi& ep, hipStream_t s) {
-  return launch_tile<T, 128, 128>(epi, A, W, N, K, m_upper, meta, ep, s);
+// fp32 configurations use this kernel; bf16 uses the tuned kernel in k_gemm_bf16.hip.
+template <>
+hipError_t launch_gemm<float>(int epi, const float* A, const float* W, int N, int K, int m_upper,
+                              const int* meta, const GemmEpi& ep, hipStream_t s) {
+  return launch_tile<float, 128, 128>(epi, A, W, N, K, m_upper, meta, ep, s);
 }
-
-template hipError_t launch_gemm<float>(int, const float*, const float*, int, int, int, const int*, const GemmEpi&, hipStream_t);
-template hipError_t launch_gemm<bf16>(int, const bf16*, const bf16*, int, int, int, const int*, const GemmEpi&, hipStream_t);
 
 }  // namespace mor

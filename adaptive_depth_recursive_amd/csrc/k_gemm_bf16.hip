@@ -1,0 +1,256 @@
+// bf16 projections of the Llama block on gfx950 MFMA, tiled for the CDNA4 CU.
+//
+// Same product and epilogues as the generic kernel in k_gemm.hip (C^T = W . A^T, weights on the
+// MFMA A side, fp32 accumulation; QKV+RoPE+cache write, residual add, SwiGLU), organised for
+// throughput:
+//  - operand tiles move global -> LDS with global_load_lds_dwordx4 (no register staging): one
+//    wave instruction writes 1 KB = 8 rows x 128 bytes of K, contiguous in LDS;
+//  - LDS rows are 128 bytes (64 bf16 of K) with the 16-byte chunks XOR-swizzled by
+//    (row >> 1) & 7, so the ds_read_b128 fragment reads of 16 consecutive rows hit 16 distinct
+//    bank groups;
+//  - 4 waves in 2 x 2, each owning a (BN/2) x (BM/2) block of the output: 128 x 128 at the
+//    256 x 256 tile, i.e. 64 FLOP per LDS byte read, enough to keep the matrix cores fed;
+//  - two LDS stages: the loads of step k+1 are in flight while step k is multiplied;
+//  - workgroups are renumbered so that the ones sharing an activation tile land on one XCD
+//    (the hardware deals workgroups round-robin over the 8 XCDs, each with its own L2).
+#include <cstdlib>
+#include <cstring>
+
+#include "mor_internal.h"
+
+namespace mor {
+
+namespace {
+
+constexpr int kRowBytes = 128;                    // one LDS row: 64 bf16 of K
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// Issue the loads of `rows` rows starting at global row `g0` (clamped to last_row) into the
+// LDS region `dst` (row-major, swizzled). Rows are split over the 4 waves, 8 per instruction.
+template <int ROWS>
+__device__ __forceinline__ void load_rows(const bf16* __restrict__ src, int ld, int g0,
+                                          int last_row, int k0, char* dst, int wave, int lane) {
+  constexpr int INSTR = ROWS / 8 / 4;             // instructions per wave
+#pragma unroll
+  for (int i = 0; i < INSTR; ++i) {
+    const int rb = (i * 4 + wave) * 8;            // first row of this wave instruction
+    const int r = rb + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);            // global 16-byte chunk that lands at slot lane&7
+    const int gr = min(g0 + r, last_row);
+    const bf16* gp = src + (size_t)gr * ld + k0 + c * 8;
+    __builtin_amdgcn_global_load_lds(gp, (lds_void*)(dst + rb * kRowBytes), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ bf16x8 frag(const char* base, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(base + row * kRowBytes + ((chunk ^ swz(row)) << 4));
+}
+
+}  // namespace
+
+template <int BN, int BM, int EPI>
+__global__ __launch_bounds__(256, 1) void k_gemm_bf16(const bf16* __restrict__ A,
+                                                      const bf16* __restrict__ W, int N, int K,
+                                                      int tiles_n, const int* __restrict__ meta,
+                                                      GemmEpi ep) {
+  constexpr int WN = BN / 2, WM = BM / 2;
+  constexpr int FN = WN / 16, FM = WM / 16;
+  constexpr int STAGE = (BN + BM) * kRowBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int M = meta[0];
+  // XCD-aware renumbering: blocks b, b+8, b+16, ... run on one XCD; give them consecutive tiles.
+  const int nblk = gridDim.x;
+  const int bid = blockIdx.x;
+  const int per_xcd = nblk / 8, rem = nblk % 8;
+  const int xcd = bid % 8, slot = bid / 8;
+  const int tile = (xcd < rem ? xcd * (per_xcd + 1) : rem * (per_xcd + 1) + (xcd - rem) * per_xcd) + slot;
+  const int tm = tile / tiles_n, tn = tile % tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  if (m0 >= M) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave >> 1, wm = wave & 1;
+  const int fr = lane & 15, g = lane >> 4;
+
+  f32x4 acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / 64;
+  auto issue = [&](int kt, int buf) {
+    char* st = smem + buf * STAGE;
+    load_rows<BN>(W, K, n0, N - 1, kt * 64, st, wave, lane);
+    load_rows<BM>(A, K, m0, M - 1, kt * 64, st + BN * kRowBytes, wave, lane);
+  };
+  issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+    const char* sw = smem + (kt & 1) * STAGE;
+    const char* sa = sw + BN * kRowBytes;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 a[FN], b[FM];
+#pragma unroll
+      for (int i = 0; i < FN; ++i) a[i] = frag(sw, wn * WN + i * 16 + fr, ks * 4 + g);
+#pragma unroll
+      for (int j = 0; j < FM; ++j) b[j] = frag(sa, wm * WM + j * 16 + fr, ks * 4 + g);
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // ------------------------------------------------------------------ epilogues
+  const int g4 = g * 4;
+  const int nw = n0 + wn * WN;
+  const int mw = m0 + wm * WM + fr;
+  if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int m = mw + 16 * j;
+      if (m >= M) continue;
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        const int n = nw + 16 * i + g4;
+        if (n >= N) continue;
+        float4* px = reinterpret_cast<float4*>(ep.x + (size_t)m * ep.ldx + n);
+        float4 v = *px;
+        v.x += acc[i][j][0]; v.y += acc[i][j][1]; v.z += acc[i][j][2]; v.w += acc[i][j][3];
+        *px = v;
+      }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int m = mw + 16 * j;
+      if (m >= M) continue;
+#pragma unroll
+      for (int i = 0; i < FN; i += 2) {
+        const int np = nw + 16 * i;
+        if (np >= N) continue;
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gt = acc[i][j][e], up = acc[i + 1][j][e];
+          o[e] = gt / (1.f + __expf(-gt)) * up;
+        }
+        Vec4<bf16>::store(reinterpret_cast<bf16*>(ep.h) + (size_t)m * ep.ldh + (np >> 1) + g4,
+                          o[0], o[1], o[2], o[3]);
+      }
+    }
+  } else {  // EPI_QKV, head_dim 64: the rotate-half partner of frag i is frag i + 2
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int m = mw + 16 * j;
+      if (m >= M) continue;
+      const int pos = ep.rowpos[m];
+      const int bseq = ep.rowseq[m], bidx = ep.rowidx[m];
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        const int nf = nw + 16 * i;
+        if (nf >= N) continue;
+        if (nf < ep.nq + ep.nkv) {
+          if ((i & 3) >= 2) continue;               // second half: written with its partner
+          const int rbase = nf < ep.nq ? 0 : ep.nq;
+          const int c0 = (nf - rbase) & 63;         // 0 or 16
+          float lo[4], hi[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int f = c0 + g4 + e;
+            const float cs = ep.rope_cos[pos * 32 + f], sn = ep.rope_sin[pos * 32 + f];
+            const float x1 = acc[i][j][e], x2 = acc[i + 2][j][e];
+            lo[e] = x1 * cs - x2 * sn;
+            hi[e] = x2 * cs + x1 * sn;
+          }
+          bf16* dst;
+          if (nf < ep.nq) {
+            dst = reinterpret_cast<bf16*>(ep.q) + (size_t)m * ep.ldq + nf + g4;
+          } else {
+            dst = reinterpret_cast<bf16*>(ep.k) + ((size_t)bseq * ep.kpad + bidx) * ep.nkv + (nf - ep.nq) + g4;
+          }
+          Vec4<bf16>::store(dst, lo[0], lo[1], lo[2], lo[3]);
+          Vec4<bf16>::store(dst + 32, hi[0], hi[1], hi[2], hi[3]);
+        } else {
+          const int vn = nf - ep.nq - ep.nkv + g4;
+          const int kvh = vn >> 6, dc = vn & 63;
+          bf16* vp = reinterpret_cast<bf16*>(ep.vt) + (((size_t)bseq * ep.hkv + kvh) * 64 + dc) * ep.kpad + bidx;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vp[(size_t)e * ep.kpad] = (bf16)acc[i][j][e];
+        }
+      }
+    }
+  }
+}
+
+namespace {
+
+int g_forced_tile = -1;   // tuning override from MOR_GEMM_TILE ("256x256", "256x128", "128x128")
+
+int forced_tile() {
+  if (g_forced_tile == -1) {
+    g_forced_tile = 0;
+    if (const char* s = getenv("MOR_GEMM_TILE")) {
+      if (!strcmp(s, "256x256")) g_forced_tile = 1;
+      else if (!strcmp(s, "256x128")) g_forced_tile = 2;
+      else if (!strcmp(s, "128x128")) g_forced_tile = 3;
+    }
+  }
+  return g_forced_tile;
+}
+
+template <int BN, int BM>
+hipError_t launch_cfg(int epi, const bf16* A, const bf16* W, int N, int K, int m_upper,
+                      const int* meta, const GemmEpi& ep, hipStream_t s) {
+  const int tn = (N + BN - 1) / BN, tm = (m_upper + BM - 1) / BM;
+  const int nblk = tn * tm;
+  if (nblk == 0) return hipSuccess;
+  switch (epi) {
+    case EPI_QKV: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_QKV>), dim3(nblk), dim3(256), 0, s, A, W, N, K, tn, meta, ep); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_RESID>), dim3(nblk), dim3(256), 0, s, A, W, N, K, tn, meta, ep); break;
+    default: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_SWIGLU>), dim3(nblk), dim3(256), 0, s, A, W, N, K, tn, meta, ep); break;
+  }
+  return hipGetLastError();
+}
+
+// Relative cost of one tile (matrix-core time at the tile's measured efficiency: the 128 x 128
+// tile runs two workgroups per CU and hides latency best on these shapes).
+double tile_cost(int bn, int bm) {
+  const double eff = (bn == 128 && bm == 128) ? 1.0 : (bn == 256 && bm == 256) ? 0.93 : 0.85;
+  return (double)bn * bm / eff;
+}
+
+}  // namespace
+
+template <>
+hipError_t launch_gemm<bf16>(int epi, const bf16* A, const bf16* W, int N, int K, int m_upper,
+                             const int* meta, const GemmEpi& ep, hipStream_t s) {
+  if (K % 64 || N % 64) return hipErrorInvalidValue;
+  int choice = forced_tile();
+  if (choice == 0) {
+    // pick the tile with the least estimated time: whole waves of 256 workgroups x tile cost
+    const int cfgs[3][2] = {{256, 256}, {256, 128}, {128, 128}};
+    double best = 1e300;
+    for (int c = 0; c < 3; ++c) {
+      const long tiles = (long)((N + cfgs[c][0] - 1) / cfgs[c][0]) * ((m_upper + cfgs[c][1] - 1) / cfgs[c][1]);
+      const double waves = (double)((tiles + 255) / 256);
+      const double t = waves * tile_cost(cfgs[c][0], cfgs[c][1]);
+      if (t < best) { best = t; choice = c + 1; }
+    }
+  }
+  switch (choice) {
+    case 1: return launch_cfg<256, 256>(epi, A, W, N, K, m_upper, meta, ep, s);
+    case 2: return launch_cfg<256, 128>(epi, A, W, N, K, m_upper, meta, ep, s);
+    default: return launch_cfg<128, 128>(epi, A, W, N, K, m_upper, meta, ep, s);
+  }
+}
+
+}  // namespace mor

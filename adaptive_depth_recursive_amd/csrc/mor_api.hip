@@ -446,6 +446,9 @@ mor_status mor_init(const mor_config* cfg, const mor_weights* w, void* workspace
   if (e == hipSuccess) e = hipMemcpyAsync(h->rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(h->rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemsetAsync(h->err, 0, 64, s);
+  // Cache slots past a sequence's active count are read (and masked) by the attention tiles;
+  // zeroing the cache once keeps them finite.
+  if (e == hipSuccess) e = hipMemsetAsync(h->kv, 0, h->kv_half_bytes * 2 * h->nstreams, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     delete h;

@@ -44,6 +44,8 @@ struct AttnArgs {
 };
 template <typename T>
 hipError_t launch_attention(const AttnArgs& a, int B, int max_rows_per_seq, hipStream_t s);
+// bf16, head_dim 64 (k_attn_bf16.hip); grid = (query blocks of 64, B, Hkv).
+hipError_t launch_attention_bf16(const AttnArgs& a, dim3 grid, hipStream_t s);
 
 // Routing, compaction, scatter and normalisation kernels (k_route.hip).
 hipError_t launch_init_sets(int B, int T, int* act0, int* cnt0, int* meta0, int* rowpos,
