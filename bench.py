@@ -27,11 +27,11 @@ if ROOT not in sys.path:
 PEAK_BF16 = 2.5e15          # dense MFMA bf16, FLOP/s (MI355X)
 PEAK_FP32 = 157.3e12
 PEAK_HBM = 8.0e12           # B/s
-KERNEL_SOURCES = {"gate_up": "adaptive_depth_recursive_amd/csrc/k_gemm.hip",
-                  "qkv": "adaptive_depth_recursive_amd/csrc/k_gemm.hip",
-                  "o_proj": "adaptive_depth_recursive_amd/csrc/k_gemm.hip",
-                  "down": "adaptive_depth_recursive_amd/csrc/k_gemm.hip",
-                  "attention": "adaptive_depth_recursive_amd/csrc/k_attn.hip"}
+KERNEL_SOURCES = {"gate_up": "adaptive_depth_recursive_amd/csrc/k_gemm_bf16.hip",
+                  "qkv": "adaptive_depth_recursive_amd/csrc/k_gemm_bf16.hip",
+                  "o_proj": "adaptive_depth_recursive_amd/csrc/k_gemm_bf16.hip",
+                  "down": "adaptive_depth_recursive_amd/csrc/k_gemm_bf16.hip",
+                  "attention": "adaptive_depth_recursive_amd/csrc/k_attn_bf16.hip"}
 
 
 def layer_params(cfg) -> int:
