@@ -39,6 +39,8 @@ class mor_config(ctypes.Structure):
         ("routing", ctypes.c_int32), ("kv_mode", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
         ("max_batch", ctypes.c_int32), ("max_seq", ctypes.c_int32),
+        ("max_slots", ctypes.c_int32), ("kv_page_tokens", ctypes.c_int32),
+        ("kv_pages", ctypes.c_int32), ("max_requests", ctypes.c_int32),
     ]
 
 
@@ -85,6 +87,10 @@ def lib() -> ctypes.CDLL:
         L.mor_timing_enable.argtypes = [vp, i32, i32]
         L.mor_timing_read.restype = i32
         L.mor_timing_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
+        L.mor_decode_submit.restype = i32
+        L.mor_decode_submit.argtypes = [vp, i32, ctypes.POINTER(i32), vp, vp, vp, vp, vp, vp]
+        L.mor_decode_step.restype = i32
+        L.mor_decode_step.argtypes = [vp, i32, vp, ctypes.POINTER(i32)]
         L.mor_destroy.restype = None
         L.mor_destroy.argtypes = [vp]
         _lib = L
@@ -93,7 +99,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("mor_abi_version", "mor_last_error", "mor_workspace_bytes", "mor_init",
             "mor_prefill", "mor_route", "mor_kv_view", "mor_get_error_flags", "mor_timing_enable",
-            "mor_timing_read", "mor_destroy")
+            "mor_timing_read", "mor_decode_submit", "mor_decode_step", "mor_destroy")
 KERNEL_KINDS = {"qkv": 1, "attention": 2, "o_proj": 3, "gate_up": 4, "down": 5}
 
 
@@ -102,8 +108,11 @@ def _check(status: int):
         raise MorError(status, lib().mor_last_error().decode())
 
 
-def make_config(cfg, max_batch: Optional[int] = None, max_seq: Optional[int] = None) -> mor_config:
-    """A mor_config from any object with the workload configuration's attribute names."""
+def make_config(cfg, max_batch: Optional[int] = None, max_seq: Optional[int] = None,
+                max_slots: int = 0, kv_page_tokens: int = 64, kv_pages: int = 0,
+                max_requests: int = 1) -> mor_config:
+    """A mor_config from any object with the workload configuration's attribute names.
+    max_slots > 0 plans the depth-wise batched decode engine (threshold routing only)."""
     c = mor_config()
     c.d_model, c.n_q_heads, c.n_kv_heads = cfg.d_model, cfg.n_q_heads, cfg.n_kv_heads
     c.head_dim, c.d_ff, c.n_layers, c.n_rec = cfg.head_dim, cfg.d_ff, cfg.n_layers, cfg.n_rec
@@ -115,6 +124,8 @@ def make_config(cfg, max_batch: Optional[int] = None, max_seq: Optional[int] = N
     c.rms_eps, c.rope_theta = cfg.rms_eps, cfg.rope_theta
     c.max_batch = cfg.batch if max_batch is None else max_batch
     c.max_seq = cfg.seq if max_seq is None else max_seq
+    c.max_slots, c.kv_page_tokens = max_slots, kv_page_tokens
+    c.kv_pages, c.max_requests = kv_pages, max_requests
     return c
 
 
@@ -146,11 +157,12 @@ class Mor:
                   ("w_up", "wu"), ("w_down", "wd"), ("g_attn", "g_attn"), ("g_ffn", "g_ffn"))
 
     def __init__(self, cfg, weights: Dict, device="cuda", max_batch=None, max_seq=None,
-                 stream=None):
+                 stream=None, max_slots=0, kv_page_tokens=64, kv_pages=0, max_requests=1):
         import torch
         self.cfg = cfg
         self.device = torch.device(device)
-        self.c = make_config(cfg, max_batch, max_seq)
+        self.c = make_config(cfg, max_batch, max_seq, max_slots, kv_page_tokens, kv_pages,
+                             max_requests)
         wdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         self._keep: List = []
 
@@ -257,6 +269,39 @@ class Mor:
         kt = self.workspace[k - base:k - base + n * es].view(dt).view(B, kpad, Hkv, hd)
         vt = self.workspace[v - base:v - base + n * es].view(dt).view(B, Hkv, hd, kpad)
         return kt, vt
+
+    # -- depth-wise batched decode ----------------------------------------------------
+    def decode_submit(self, lengths, inputs, outputs, exit_depth, h_dump=None, z_dump=None,
+                      stream=None):
+        """mor_decode_submit: lengths is a host int sequence; inputs/outputs fp32 [tokens, d],
+        exit_depth int8 [tokens], optional h_dump [tokens, N_r+1, d] and z_dump [tokens, N_r]
+        device tensors (kept alive by this object until the next submit)."""
+        import numpy as np
+        lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+        self._dec_keep = (inputs, outputs, exit_depth, h_dump, z_dump)
+        _check(lib().mor_decode_submit(
+            self.handle, int(lens.size), lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            inputs.data_ptr(), outputs.data_ptr(), exit_depth.data_ptr(), _ptr(h_dump),
+            _ptr(z_dump), _stream(stream)))
+
+    def decode_step(self, n_iters: int, sync: bool = False, stream=None):
+        """mor_decode_step: enqueue n_iters iterations; with sync=True returns
+        (tokens finished, requests finished, iterations run)."""
+        if not sync:
+            _check(lib().mor_decode_step(self.handle, n_iters, _stream(stream), None))
+            return None
+        prog = (ctypes.c_int32 * 3)()
+        _check(lib().mor_decode_step(self.handle, n_iters, _stream(stream), prog))
+        return prog[0], prog[1], prog[2]
+
+    def decode_run(self, total_tokens: int, chunk: int = 32, max_iters: int = 1 << 22, stream=None):
+        """Steps until every submitted token is finished; returns the iterations run."""
+        it = 0
+        while True:
+            done, _, iters = self.decode_step(chunk, sync=True, stream=stream)
+            it = iters
+            if done >= total_tokens or it >= max_iters:
+                return it
 
     def timing_enable(self, kind: str, max_launches: int):
         _check(lib().mor_timing_enable(self.handle, KERNEL_KINDS[kind] if kind else 0, max_launches))

@@ -1,0 +1,632 @@
+// Depth-wise batched MoR decode on gfx950 (reading notes section 4, continuous depth-wise
+// batching; MoR paper A.3 and reading notes 3.1 / 3.2 for the per-recursion caches; reading notes
+// 2.1 for the static sigmoid > 0.5 exit test used at inference).
+//
+// Every iteration advances each occupied slot by one recursion: a newly admitted token first runs
+// the unique first layer, then every occupied slot runs the n_s shared layers at its own
+// recursion depth (the tokens at different depths share the same weights, so they share every
+// launch), then tokens whose next router logit is not positive -- or that reached N_r -- run the
+// unique last layer and leave. A finished token's slot takes the request's next token, a finished
+// request's slot takes the next request from the FIFO. All of this state lives on the device, so
+// an iteration needs no host round trip.
+//
+// Slots are the rows of every decode GEMM (at most 64); rows whose slot takes no part in a layer
+// are computed and ignored, so the launches have fixed grids.
+//
+// KV cache: pages of P tokens for one layer of one stream, K then V, each [hkv][P][hd]. Layer
+// stream 0 = first layer, 1 = last layer, 2 + (r-1) n_s + (j-1) = shared layer j at recursion r.
+// A page table per (slot, layer stream) maps the index of a cached token to its page. Pages come
+// from a device free-list stack and return to it when the request finishes.
+#include <algorithm>
+#include <climits>
+
+#include "mor_internal.h"
+
+namespace mor {
+
+namespace {
+
+__device__ __forceinline__ int wave_scan_excl(int v, int* total) {
+  const int lane = lane_id();
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  *total = __shfl(x, 63);
+  return x - v;
+}
+
+__device__ __forceinline__ int layer_stream_shared(const DecArgs& a, int r, int j) {
+  return 2 + (r - 1) * a.n_s + (j - 1);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ scheduler (one wave)
+// Lane s owns slot s. Order of work: finish the tokens that left last iteration (advance to the
+// next position, or finish the request and return its pages), admit queued requests into free
+// slots in slot order, then allocate the pages this iteration's KV appends need.
+__global__ __launch_bounds__(64) void k_dec_schedule(DecArgs a) {
+  const int s = lane_id();
+  const bool valid = s < a.S;
+  int* g = a.glob;
+  if (g[G_HALT]) {
+    if (valid) { a.sl_first[s] = 0; a.sl_part[s] = 0; a.sl_exit[s] = 0; }
+    return;
+  }
+  const int nreq = g[G_NREQ];
+  int req = valid ? a.sl_req[s] : -1;
+  int pos = valid ? a.sl_pos[s] : 0;
+  int depth = valid ? a.sl_depth[s] : 0;
+  bool admit = false;
+  int nfree = 0;
+  bool finished = false;
+  if (valid && req >= 0 && depth == 0) {
+    if (pos + 1 < a.req_len[req]) {
+      pos += 1;
+      admit = true;
+    } else {
+      finished = true;
+      const int len = a.req_len[req];
+      nfree = 2 * ((len + a.P - 1) / a.P);
+      for (int r = 1; r <= a.R; ++r)
+        if (!a.kv_share || r == 1) nfree += a.n_s * ((a.sl_cnt[s * a.R + r - 1] + a.P - 1) / a.P);
+    }
+  }
+  // return pages of finished requests (stack order: slot, layer stream, page index)
+  int tot_free;
+  const int top0 = g[G_TOP];
+  int w = top0 + wave_scan_excl(nfree, &tot_free);
+  if (finished) {
+    for (int ls = 0; ls < a.LS; ++ls) {
+      int n;
+      if (ls < 2) {
+        n = (a.req_len[req] + a.P - 1) / a.P;
+      } else {
+        const int r = (ls - 2) / a.n_s + 1;
+        n = (a.kv_share && r > 1) ? 0 : (a.sl_cnt[s * a.R + r - 1] + a.P - 1) / a.P;
+      }
+      const int* pt = a.ptab + ((size_t)s * a.LS + ls) * a.pps;
+      for (int i = 0; i < n; ++i) a.free_pages[w++] = pt[i];
+    }
+    req = -1;
+  }
+  int top = top0 + tot_free;
+
+  // admit queued requests into free slots, in slot order
+  const bool isfree = valid && req < 0;
+  int nfreeslots;
+  const int rank = wave_scan_excl(isfree ? 1 : 0, &nfreeslots);
+  const int next = g[G_NEXT];
+  if (isfree && next + rank < nreq) {
+    req = next + rank;
+    pos = 0;
+    admit = true;
+    for (int r = 0; r < a.R; ++r) a.sl_cnt[s * a.R + r] = 0;
+  }
+  const int taken = min(nfreeslots, max(0, nreq - next));
+
+  const bool part = valid && req >= 0;
+  const int r = admit ? 1 : depth;
+  int need = 0;
+  bool need_u = false, need_s = false;
+  if (part) {
+    need_u = admit && (pos % a.P == 0);
+    need_s = (!a.kv_share || r == 1) && (a.sl_cnt[s * a.R + r - 1] % a.P == 0);
+    need = (need_u ? 2 : 0) + (need_s ? a.n_s : 0);
+  }
+  int tot_need;
+  int off = wave_scan_excl(need, &tot_need);
+  const bool full = tot_need > top;
+  if (!full && part) {
+    int p = top - tot_need + off;
+    if (need_u) {
+      a.ptab[((size_t)s * a.LS + 0) * a.pps + pos / a.P] = a.free_pages[p++];
+      a.ptab[((size_t)s * a.LS + 1) * a.pps + pos / a.P] = a.free_pages[p++];
+    }
+    if (need_s) {
+      const int idx = a.sl_cnt[s * a.R + r - 1] / a.P;
+      for (int j = 1; j <= a.n_s; ++j)
+        a.ptab[((size_t)s * a.LS + layer_stream_shared(a, r, j)) * a.pps + idx] = a.free_pages[p++];
+    }
+  }
+  if (valid) {
+    a.sl_req[s] = req;
+    a.sl_pos[s] = pos;
+    a.sl_depth[s] = part ? r : 0;
+    a.sl_first[s] = (!full && admit) ? 1 : 0;
+    a.sl_part[s] = (!full && part) ? 1 : 0;
+    a.sl_exit[s] = 0;
+  }
+  if (s == 0) {
+    g[G_NEXT] = next + taken;
+    g[G_ITER] += 1;
+    if (full) {
+      g[G_HALT] = 1;
+      g[G_TOP] = top;
+      atomicOr(a.err, (unsigned)ERR_KV_FULL);
+    } else {
+      g[G_TOP] = top - tot_need;
+    }
+  }
+}
+
+hipError_t launch_dec_schedule(const DecArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_dec_schedule, dim3(1), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+// Engine reset for a new set of requests: empty slots, full free-page stack, zero counters.
+__global__ void k_dec_reset(DecArgs a, int n_req) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < a.kv_pages) a.free_pages[i] = a.kv_pages - 1 - i;
+  if (i < a.S) {
+    a.sl_req[i] = -1; a.sl_pos[i] = 0; a.sl_depth[i] = 0;
+    a.sl_first[i] = 0; a.sl_part[i] = 0; a.sl_exit[i] = 0;
+    for (int r = 0; r < a.R; ++r) a.sl_cnt[i * a.R + r] = 0;
+  }
+  if (i < 64) a.gate[i] = 0.f;
+  if (i < 64 * a.d) { a.X[i] = 0.f; a.Hs[i] = 0.f; }
+  if (i < G_COUNT) a.glob[i] = (i == G_TOP) ? a.kv_pages : (i == G_NREQ) ? n_req : 0;
+}
+
+hipError_t launch_dec_reset(const DecArgs& a, int n_req, hipStream_t s) {
+  const long n = std::max<long>(std::max<long>(a.kv_pages, 64L * a.d), G_COUNT);
+  hipLaunchKernelGGL(k_dec_reset, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, n_req);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ RMSNorm of the slot rows
+// One wave per slot row. With gather_inputs (first layer), admitted slots first load their
+// token's input hidden state into X, and every other row of X is cleared.
+template <typename T>
+__global__ __launch_bounds__(256) void k_dec_norm(DecArgs a, int gather, const float* __restrict__ g,
+                                                  float eps, T* __restrict__ Xn) {
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  if (s >= a.S) return;
+  const int d = a.d;
+  float4* x = reinterpret_cast<float4*>(a.X + (size_t)s * d);
+  if (gather) {
+    if (a.sl_first[s]) {
+      const int tok = a.req_off[a.sl_req[s]] + a.sl_pos[s];
+      const float4* src = reinterpret_cast<const float4*>(a.inputs + (size_t)tok * d);
+      for (int c = lane; c < d / 4; c += WAVE) x[c] = src[c];
+    } else {
+      for (int c = lane; c < d / 4; c += WAVE) x[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  float ss = 0.f;
+  for (int c = lane; c < d / 4; c += WAVE) {
+    const float4 v = x[c];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  const float rinv = 1.f / sqrtf(ss / (float)d + eps);
+  T* out = Xn + (size_t)s * d;
+  for (int c = lane; c < d / 4; c += WAVE) {
+    const float4 v = x[c], gg = g4[c];
+    Vec4<T>::store(out + 4 * c, v.x * rinv * gg.x, v.y * rinv * gg.y, v.z * rinv * gg.z,
+                   v.w * rinv * gg.w);
+  }
+}
+
+template <typename T>
+hipError_t launch_dec_norm(const DecArgs& a, bool gather_inputs, const float* g, float eps, T* Xn,
+                           hipStream_t s) {
+  hipLaunchKernelGGL((k_dec_norm<T>), dim3((a.S + 3) / 4), dim3(256), 0, s, a, gather_inputs ? 1 : 0,
+                     g, eps, Xn);
+  return hipGetLastError();
+}
+template hipError_t launch_dec_norm<float>(const DecArgs&, bool, const float*, float, float*, hipStream_t);
+template hipError_t launch_dec_norm<bf16>(const DecArgs&, bool, const float*, float, bf16*, hipStream_t);
+
+// ------------------------------------------------------------------ recursion entry / exit
+// Fixed-order router logit of a row (the order of k_router): returns the value in every lane.
+__device__ __forceinline__ float dec_logit(const float* __restrict__ h, const float* __restrict__ w,
+                                           const float* bias, int d, int lane) {
+  float p = 0.f;
+  for (int i = lane; i < d; i += WAVE) p = add_rn(p, mul_rn(h[i], w[i]));
+  p = fold_fixed(p);
+  if (bias) p = add_rn(p, bias[0]);
+  return (p == 0.f) ? 0.f : p;
+}
+
+// Start of the recursion of every occupied slot: a newly admitted token's state is the first
+// layer's output, a continuing token's state is carried in Hs; the shared block works on X.
+// The gate of the recursion is sigmoid(theta_r . H + b_r).
+__global__ __launch_bounds__(256) void k_dec_prep(DecArgs a) {
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  if (s >= a.S || !a.sl_part[s]) return;
+  const int d = a.d, r = a.sl_depth[s];
+  float* x = a.X + (size_t)s * d;
+  float* hs = a.Hs + (size_t)s * d;
+  const int tok = a.req_off[a.sl_req[s]] + a.sl_pos[s];
+  if (a.sl_first[s]) {
+    for (int c = lane; c < d; c += WAVE) hs[c] = x[c];
+    if (a.h_dump)
+      for (int c = lane; c < d; c += WAVE) a.h_dump[((size_t)tok * (a.R + 1)) * d + c] = x[c];
+  } else {
+    for (int c = lane; c < d; c += WAVE) x[c] = hs[c];
+  }
+  const float z = dec_logit(hs, a.router_w + (size_t)(r - 1) * d, a.router_b + (r - 1), d, lane);
+  if (lane == 0) {
+    if (z != z) atomicOr(a.err, (unsigned)ERR_NAN_LOGIT);
+    a.gate[s] = a.unit_gate ? -1.f : 1.f / (1.f + __expf(-z));
+    if (a.z_dump) a.z_dump[(size_t)tok * a.R + (r - 1)] = z;
+  }
+}
+
+hipError_t launch_dec_prep(const DecArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_dec_prep, dim3((a.S + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// End of the recursion: H <- H + g (F(H) - H) (or F(H) under unit gating), then the exit test on
+// the next router logit: the token continues iff r < N_r and theta_{r+1} . H + b_{r+1} > 0.
+__global__ __launch_bounds__(256) void k_dec_update(DecArgs a) {
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  if (s >= a.S || !a.sl_part[s]) return;
+  const int d = a.d, r = a.sl_depth[s];
+  const float g = a.gate[s];
+  float* x = a.X + (size_t)s * d;
+  float* hs = a.Hs + (size_t)s * d;
+  const int tok = a.req_off[a.sl_req[s]] + a.sl_pos[s];
+  const float* w = (r < a.R) ? a.router_w + (size_t)r * d : nullptr;
+  float p = 0.f;
+  for (int c = lane; c < d; c += WAVE) {
+    const float hv = hs[c], xv = x[c];
+    const float hn = (g < 0.f) ? xv : hv + g * (xv - hv);
+    hs[c] = hn;
+    x[c] = hn;
+    if (a.h_dump) a.h_dump[((size_t)tok * (a.R + 1) + r) * d + c] = hn;
+    if (w) p = add_rn(p, mul_rn(hn, w[c]));
+  }
+  bool leave = true;
+  if (w) {
+    p = fold_fixed(p);
+    p = add_rn(p, a.router_b[r]);
+    p = (p == 0.f) ? 0.f : p;
+    leave = !(p > 0.f);
+    if (lane == 0) {
+      if (p != p) atomicOr(a.err, (unsigned)ERR_NAN_LOGIT);
+      if (a.z_dump) a.z_dump[(size_t)tok * a.R + r] = p;
+    }
+  }
+  if (lane == 0) {
+    a.sl_cnt[s * a.R + r - 1] += 1;
+    if (leave) {
+      a.sl_exit[s] = 1;
+      a.exit_depth[tok] = (signed char)r;
+    } else {
+      a.sl_depth[s] = r + 1;
+    }
+  }
+}
+
+hipError_t launch_dec_update(const DecArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_dec_update, dim3((a.S + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Tokens that ran the last layer: write the output row, mark the token finished.
+__global__ __launch_bounds__(256) void k_dec_output(DecArgs a) {
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  if (s >= a.S || !a.sl_exit[s]) return;
+  const int d = a.d;
+  const int tok = a.req_off[a.sl_req[s]] + a.sl_pos[s];
+  const float4* x = reinterpret_cast<const float4*>(a.X + (size_t)s * d);
+  float4* o = reinterpret_cast<float4*>(a.outputs + (size_t)tok * d);
+  for (int c = lane; c < d / 4; c += WAVE) o[c] = x[c];
+  if (lane == 0) {
+    a.sl_depth[s] = 0;
+    a.sl_exit[s] = 0;
+    atomicAdd(&a.glob[G_TOKENS], 1);
+    if (a.sl_pos[s] + 1 == a.req_len[a.sl_req[s]]) atomicAdd(&a.glob[G_REQS], 1);
+  }
+}
+
+hipError_t launch_dec_output(const DecArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_dec_output, dim3((a.S + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ decode attention
+// One workgroup per (slot, KV head). It rotates the slot's new query heads and key (RoPE at the
+// token's position, fp32, then rounded to the element type), appends the new K/V to the slot's
+// page of the layer stream, and attends over the cached keys of that stream plus the new one:
+// recursion-wise caching reads the stream of the token's own recursion; recursive KV sharing at
+// r >= 2 appends nothing and reads the recursion-1 stream of the same shared layer.
+// Waves take 64-key tiles in turn (lane = key for the scores, lane = head-dim element for PV)
+// and are merged in wave order at the end.
+template <typename T, int HD, int G>
+__global__ __launch_bounds__(256) void k_dec_attn(DecArgs a, int kind, int j) {
+  constexpr int KT = 64;
+  __shared__ float sq[G][HD];
+  __shared__ float skn[HD], svn[HD];
+  __shared__ float sp[4][G][KT];
+  __shared__ float sm[4][G], sl[4][G];
+  __shared__ float sacc[4][G][HD];
+
+  const int s = blockIdx.x, kvh = blockIdx.y;
+  if (s >= a.S) return;
+  const int part = kind == DL_FIRST ? a.sl_first[s] : kind == DL_LAST ? a.sl_exit[s] : a.sl_part[s];
+  if (!part) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pos = a.sl_pos[s], r = a.sl_depth[s];
+  int ls_w, ls_r, idx_w, nkeys;
+  if (kind == DL_FIRST || kind == DL_LAST) {
+    ls_w = ls_r = (kind == DL_FIRST) ? 0 : 1;
+    idx_w = pos;
+    nkeys = pos;
+  } else if (a.kv_share && r >= 2) {
+    ls_w = -1;
+    ls_r = layer_stream_shared(a, 1, j);
+    idx_w = 0;
+    nkeys = a.sl_cnt[s * a.R + 0];
+  } else {
+    ls_w = ls_r = layer_stream_shared(a, r, j);
+    idx_w = a.sl_cnt[s * a.R + r - 1];
+    nkeys = idx_w;
+  }
+  const int half = HD / 2;
+  const float* qkv = a.qkv + (size_t)s * a.nqkv;
+  for (int i = tid; i < (G + 2) * HD; i += 256) {
+    const int hh = i / HD, c = i % HD;
+    const int pc = c < half ? c + half : c - half;
+    const float* base;
+    if (hh < G) base = qkv + (kvh * G + hh) * HD;
+    else if (hh == G) base = qkv + a.nq + kvh * HD;
+    else base = qkv + a.nq + a.nkv + kvh * HD;
+    float v = base[c];
+    if (hh <= G) {
+      const int f = c % half;
+      const float cs = a.rope_cos[pos * half + f], sn = a.rope_sin[pos * half + f];
+      v = c < half ? v * cs - base[pc] * sn : v * cs + base[pc] * sn;
+    }
+    v = to_f32(from_f32<T>(v));
+    if (hh < G) sq[hh][c] = v;
+    else if (hh == G) skn[c] = v;
+    else svn[c] = v;
+  }
+  __syncthreads();
+  T* pool = reinterpret_cast<T*>(a.pool);
+  const size_t vofs = (size_t)a.hkv * a.P * HD;
+  if (ls_w >= 0 && tid < 2 * HD) {
+    const int page = a.ptab[((size_t)s * a.LS + ls_w) * a.pps + idx_w / a.P];
+    T* dst = pool + (size_t)page * a.page_elems + ((size_t)kvh * a.P + idx_w % a.P) * HD;
+    if (tid < HD) dst[tid] = from_f32<T>(skn[tid]);
+    else dst[vofs + tid - HD] = from_f32<T>(svn[tid - HD]);
+  }
+
+  const float sl2 = a.scale_log2;
+  float m[G], l[G], acc[G];
+  const bool lane_c = lane < HD;
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) { m[hh] = -INFINITY; l[hh] = 0.f; acc[hh] = 0.f; }
+  if (wave == 0 && ls_w >= 0) {            // the new key: p = exp2(0) = 1
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float dot = 0.f;
+      for (int c = 0; c < HD; ++c) dot += sq[hh][c] * skn[c];
+      m[hh] = dot * sl2;
+      l[hh] = 1.f;
+      acc[hh] = lane_c ? svn[lane] : 0.f;
+    }
+  }
+  const int* pt = a.ptab + ((size_t)s * a.LS + ls_r) * a.pps;
+  for (int t0 = wave * KT; t0 < nkeys; t0 += 4 * KT) {
+    const int i = t0 + lane;
+    const bool valid = i < nkeys;
+    float sc[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) sc[hh] = 0.f;
+    if (valid) {
+      const T* kr = pool + (size_t)pt[i / a.P] * a.page_elems + ((size_t)kvh * a.P + i % a.P) * HD;
+      constexpr int CH = 16 / (int)sizeof(T);
+#pragma unroll
+      for (int c0 = 0; c0 < HD; c0 += CH) {
+        union { uint4 u; T e[CH]; } kc;
+        kc.u = *reinterpret_cast<const uint4*>(kr + c0);
+#pragma unroll
+        for (int e = 0; e < CH; ++e) {
+          const float kv = to_f32(kc.e[e]);
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) sc[hh] += sq[hh][c0 + e] * kv;
+        }
+      }
+    }
+    const int nt = min(KT, nkeys - t0);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float v = valid ? sc[hh] * sl2 : -INFINITY;
+      float mt = v;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o));
+      const float mn = fmaxf(m[hh], mt);
+      const float alpha = exp2f(m[hh] - mn);
+      const float p = valid ? exp2f(v - mn) : 0.f;
+      l[hh] = l[hh] * alpha + wave_sum(p);
+      acc[hh] *= alpha;
+      m[hh] = mn;
+      sp[wave][hh][lane] = to_f32(from_f32<T>(p));
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    if (lane_c) {
+      for (int kk = 0; kk < nt; ++kk) {
+        const int ik = t0 + kk;
+        const T* vr = pool + (size_t)pt[ik / a.P] * a.page_elems + vofs + ((size_t)kvh * a.P + ik % a.P) * HD;
+        const float vv = to_f32(vr[lane]);
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) acc[hh] += sp[wave][hh][kk] * vv;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    if (lane == 0) { sm[wave][hh] = m[hh]; sl[wave][hh] = l[hh]; }
+    if (lane_c) sacc[wave][hh][lane] = acc[hh];
+  }
+  __syncthreads();
+  if (wave == 0 && lane_c) {
+    T* out = reinterpret_cast<T*>(a.o) + (size_t)s * a.nq;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float M = -INFINITY;
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][hh]);
+      float L = 0.f, o = 0.f;
+      for (int w = 0; w < 4; ++w) {
+        const float f = (sm[w][hh] == -INFINITY) ? 0.f : exp2f(sm[w][hh] - M);
+        L += sl[w][hh] * f;
+        o += sacc[w][hh][lane] * f;
+      }
+      out[(kvh * G + hh) * HD + lane] = from_f32<T>(o / L);
+    }
+  }
+}
+
+template <typename T, int HD>
+static hipError_t dec_attn_g(const DecArgs& a, int kind, int j, hipStream_t s) {
+  dim3 grid(a.S, a.hkv);
+  switch (a.hq / a.hkv) {
+    case 1: hipLaunchKernelGGL((k_dec_attn<T, HD, 1>), grid, dim3(256), 0, s, a, kind, j); break;
+    case 2: hipLaunchKernelGGL((k_dec_attn<T, HD, 2>), grid, dim3(256), 0, s, a, kind, j); break;
+    case 3: hipLaunchKernelGGL((k_dec_attn<T, HD, 3>), grid, dim3(256), 0, s, a, kind, j); break;
+    case 4: hipLaunchKernelGGL((k_dec_attn<T, HD, 4>), grid, dim3(256), 0, s, a, kind, j); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dec_attn(const DecArgs& a, int kind, int j, hipStream_t s) {
+  switch (a.hd) {
+    case 16: return dec_attn_g<T, 16>(a, kind, j, s);
+    case 32: return dec_attn_g<T, 32>(a, kind, j, s);
+    case 64: return dec_attn_g<T, 64>(a, kind, j, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+template hipError_t launch_dec_attn<float>(const DecArgs&, int, int, hipStream_t);
+template hipError_t launch_dec_attn<bf16>(const DecArgs&, int, int, hipStream_t);
+
+// ------------------------------------------------------------------ skinny projections
+// out^T = W . A^T for the 64 rows of A (the slots), weights on the MFMA A side. A workgroup owns
+// RG groups of 16 weight rows; its 4 waves take interleaved 128-byte slices of K, multiply all
+// 64 slot rows, and the partial sums are added in wave order in LDS (deterministic). Wave w then
+// finishes slot rows 16w..16w+15: each lane holds 4 consecutive output columns of one row.
+template <typename T, int RG, int EPI>
+__global__ __launch_bounds__(256) void k_skinny(const T* __restrict__ A, const T* __restrict__ W,
+                                                int N, int K, int M, SkinnyEpi ep) {
+  typedef Mma<T> MM;
+  constexpr int UK = 128 / (int)sizeof(T);          // K elements per slice
+  constexpr int NS = UK / MM::KSTEP;               // MFMA steps per slice
+  __shared__ f32x4 red[4][RG][4][64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 16 * RG;
+  f32x4 acc[RG][4];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf) acc[rg][mf] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nu = K / UK;
+  const T* wrow[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) wrow[rg] = W + (size_t)(n0 + 16 * rg + fr) * K + g * MM::KW;
+  const T* arow[4];
+#pragma unroll
+  for (int mf = 0; mf < 4; ++mf) arow[mf] = A + (size_t)(16 * mf + fr) * K + g * MM::KW;
+
+  for (int u = wave; u < nu; u += 4) {
+    typename MM::frag wa[RG][NS], xb[4][NS];
+#pragma unroll
+    for (int ks = 0; ks < NS; ++ks) {
+      const int k = u * UK + ks * MM::KSTEP;
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) wa[rg][ks] = MM::load(wrow[rg] + k);
+#pragma unroll
+      for (int mf = 0; mf < 4; ++mf) xb[mf][ks] = MM::load(arow[mf] + k);
+    }
+#pragma unroll
+    for (int ks = 0; ks < NS; ++ks)
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) acc[rg][mf] = MM::mma(wa[rg][ks], xb[mf][ks], acc[rg][mf]);
+  }
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf) red[wave][rg][mf][lane] = acc[rg][mf];
+  __syncthreads();
+  const int mf = wave;
+  f32x4 v[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    v[rg] = red[0][rg][mf][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v[rg] += red[w][rg][mf][lane];
+  }
+  const int m = 16 * mf + fr;
+  if (m >= M) return;
+  if constexpr (EPI == SK_STORE) {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      const int n = n0 + 16 * rg + 4 * g;
+      *reinterpret_cast<float4*>(ep.out + (size_t)m * ep.ldo + n) =
+          make_float4(v[rg][0], v[rg][1], v[rg][2], v[rg][3]);
+    }
+  } else if constexpr (EPI == SK_RESID) {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      const int n = n0 + 16 * rg + 4 * g;
+      float4* px = reinterpret_cast<float4*>(ep.x + (size_t)m * ep.ldx + n);
+      float4 x = *px;
+      x.x += v[rg][0]; x.y += v[rg][1]; x.z += v[rg][2]; x.w += v[rg][3];
+      *px = x;
+    }
+  } else {  // SK_SWIGLU: weight rows are gate/up groups of 16 (RG == 2)
+    const int col = (n0 >> 1) + 4 * g;
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float gt = v[0][e], up = v[1][e];
+      o[e] = gt / (1.f + __expf(-gt)) * up;
+    }
+    Vec4<T>::store(reinterpret_cast<T*>(ep.h) + (size_t)m * ep.ldh + col, o[0], o[1], o[2], o[3]);
+  }
+}
+
+template <typename T>
+hipError_t launch_skinny(int epi, const T* A, const T* W, int N, int K, int M, const SkinnyEpi& ep,
+                         hipStream_t s) {
+  if (K % 64 || N % 32 || M > 64) return hipErrorInvalidValue;
+  switch (epi) {
+    case SK_STORE:
+      hipLaunchKernelGGL((k_skinny<T, 1, SK_STORE>), dim3(N / 16), dim3(256), 0, s, A, W, N, K, M, ep);
+      break;
+    case SK_RESID:
+      hipLaunchKernelGGL((k_skinny<T, 1, SK_RESID>), dim3(N / 16), dim3(256), 0, s, A, W, N, K, M, ep);
+      break;
+    default:
+      hipLaunchKernelGGL((k_skinny<T, 2, SK_SWIGLU>), dim3(N / 32), dim3(256), 0, s, A, W, N, K, M, ep);
+      break;
+  }
+  return hipGetLastError();
+}
+template hipError_t launch_skinny<float>(int, const float*, const float*, int, int, int, const SkinnyEpi&, hipStream_t);
+template hipError_t launch_skinny<bf16>(int, const bf16*, const bf16*, int, int, int, const SkinnyEpi&, hipStream_t);
+
+}  // namespace mor

@@ -9,6 +9,7 @@
 //                   KV sharing), gated scatter back into H fused with the router of r+1
 //   last layer on all tokens.
 // Expert-choice counts are static, so nothing is read back to the host during a call.
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -88,6 +89,18 @@ struct mor_handle_s {
   int* rows = nullptr;           // 4 x [MT]: the same for the current active set
   float* gate = nullptr;         // [MT]
   unsigned* err = nullptr;
+  // depth-wise batched decode
+  bool decode = false;
+  int kv_pages = 0, pps = 0, LS = 0;
+  size_t page_bytes = 0;
+  DecArgs dec{};
+  int* dreq_len = nullptr;       // [max_requests]
+  int* dreq_off = nullptr;       // [max_requests]
+  void* dXn = nullptr;           // [64][d]
+  float* dQkv = nullptr;         // [64][nqkv]
+  void* dO = nullptr;            // [64][nq]
+  void* dHf = nullptr;           // [64][d_ff]
+  bool submitted = false;
   // measurement: HIP events around every launch of one kernel kind
   int timing_kind = 0;
   std::vector<hipEvent_t> ev;
@@ -128,6 +141,13 @@ mor_status validate(const mor_config* c) {
   if ((double)c->max_batch * c->max_seq * (double)std::max(c->d_ff, c->d_model) > 2.0e9)
     return fail(MOR_E_SHAPE, "max_batch * max_seq too large");
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail(MOR_E_INVALID, "rms_eps / rope_theta");
+  if (c->max_slots < 0 || c->max_slots > 64) return fail(MOR_E_SHAPE, "max_slots must be 0..64");
+  if (c->max_slots > 0) {
+    if (c->routing != MOR_ROUTE_THRESHOLD) return fail(MOR_E_INVALID, "decode needs threshold routing");
+    const int P = c->kv_page_tokens;
+    if (P != 16 && P != 32 && P != 64 && P != 128) return fail(MOR_E_SHAPE, "kv_page_tokens must be 16, 32, 64 or 128");
+    if (c->kv_pages < 0 || c->max_requests < 1) return fail(MOR_E_INVALID, "kv_pages >= 0, max_requests >= 1");
+  }
   return MOR_OK;
 }
 
@@ -173,6 +193,37 @@ size_t plan(const mor_config& c, mor_handle_s* h, char* base) {
   int* rows = cur.take<int>(4 * MT * 4);
   float* gate = cur.take<float>(MT * 4);
   unsigned* err = cur.take<unsigned>(64);
+  // decode engine
+  const int S = c.max_slots;
+  const int P = S ? c.kv_page_tokens : 1;
+  const int pps = ceil_div(c.max_seq, P);
+  const int LS = 2 + R * n_s;
+  const size_t page_elems = 2 * nkv * (size_t)P;
+  const size_t page_bytes = page_elems * es;
+  const int kv_pages = S ? (c.kv_pages ? c.kv_pages : S * LS * pps) : 0;
+  DecArgs da{};
+  int *dreq_len = nullptr, *dreq_off = nullptr;
+  void *dXn = nullptr, *dO = nullptr, *dHf = nullptr;
+  float* dQkv = nullptr;
+  if (S) {
+    da.sl_req = cur.take<int>(S * 4); da.sl_pos = cur.take<int>(S * 4);
+    da.sl_depth = cur.take<int>(S * 4); da.sl_first = cur.take<int>(S * 4);
+    da.sl_part = cur.take<int>(S * 4); da.sl_exit = cur.take<int>(S * 4);
+    da.sl_cnt = cur.take<int>((size_t)S * R * 4);
+    da.ptab = cur.take<int>((size_t)S * LS * pps * 4);
+    da.free_pages = cur.take<int>((size_t)kv_pages * 4);
+    da.glob = cur.take<int>(G_COUNT * 4);
+    dreq_len = cur.take<int>((size_t)c.max_requests * 4);
+    dreq_off = cur.take<int>((size_t)c.max_requests * 4);
+    da.X = cur.take<float>(64 * d * 4);
+    da.Hs = cur.take<float>(64 * d * 4);
+    da.gate = cur.take<float>(64 * 4);
+    dXn = cur.take<void>(64 * d * es);
+    dQkv = cur.take<float>(64 * nqkv * 4);
+    dO = cur.take<void>(64 * nq * es);
+    dHf = cur.take<void>(64 * dff * es);
+    da.pool = cur.take<void>((size_t)kv_pages * page_bytes);
+  }
   if (h) {
     h->n_s = n_s; h->es = (int)es; h->nq = (int)nq; h->nkv = (int)nkv; h->nqkv = (int)nqkv;
     h->kpad = (int)kpad; h->nstreams = nstreams; h->MT = MT;
@@ -183,6 +234,26 @@ size_t plan(const mor_config& c, mor_handle_s* h, char* base) {
     h->act = act; h->cnt = cnt; h->meta = meta; h->z = z; h->tc_logits = tc_logits;
     h->depth = depth; h->prob = prob; h->rows_all = rows_all; h->rows = rows; h->gate = gate;
     h->err = err;
+    h->decode = S > 0;
+    if (S) {
+      h->kv_pages = kv_pages; h->pps = pps; h->LS = LS; h->page_bytes = page_bytes;
+      h->dreq_len = dreq_len; h->dreq_off = dreq_off;
+      h->dXn = dXn; h->dQkv = dQkv; h->dO = dO; h->dHf = dHf;
+      da.S = S; da.R = R; da.n_s = n_s; da.P = P; da.pps = pps; da.LS = LS;
+      da.d = (int)d; da.hd = (int)hd; da.hkv = c.n_kv_heads; da.hq = c.n_q_heads;
+      da.nq = (int)nq; da.nkv = (int)nkv; da.nqkv = (int)nqkv;
+      da.kv_share = c.kv_mode == MOR_KV_SHARE_FIRST;
+      da.unit_gate = c.gate_mode == MOR_GATE_UNIT;
+      da.page_elems = (long long)page_elems;
+      da.kv_pages = kv_pages;
+      da.err = err;
+      da.req_len = dreq_len; da.req_off = dreq_off;
+      da.router_w = router_w; da.router_b = router_b;
+      da.rope_cos = rope_cos; da.rope_sin = rope_sin;
+      da.qkv = dQkv; da.o = dO;
+      da.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
+      h->dec = da;
+    }
   }
   return cur.off + kAlign;
 }
@@ -370,6 +441,47 @@ mor_status prefill_impl(mor_handle_s* h, const float* h_in, int B, int T, float*
   return MOR_OK;
 }
 
+// ------------------------------------------------------------------ decode iteration
+template <typename E>
+mor_status dec_layer(mor_handle_s* h, const BlockPacked& w, int kind, int j, hipStream_t s) {
+  const mor_config& c = h->cfg;
+  const DecArgs& a = h->dec;
+  const int d = c.d_model, dff = c.d_ff, S = a.S;
+  E* Xn = reinterpret_cast<E*>(h->dXn);
+  HIPCHK(launch_dec_norm<E>(a, kind == DL_FIRST, w.g_attn, c.rms_eps, Xn, s));
+  SkinnyEpi eq{};
+  eq.out = h->dQkv; eq.ldo = h->nqkv;
+  HIPCHK(launch_skinny<E>(SK_STORE, Xn, reinterpret_cast<const E*>(w.wqkv), h->nqkv, d, S, eq, s));
+  HIPCHK(launch_dec_attn<E>(a, kind, j, s));
+  SkinnyEpi er{};
+  er.x = a.X; er.ldx = d;
+  HIPCHK(launch_skinny<E>(SK_RESID, reinterpret_cast<const E*>(h->dO), reinterpret_cast<const E*>(w.wo), d, h->nq, S, er, s));
+  HIPCHK(launch_dec_norm<E>(a, false, w.g_ffn, c.rms_eps, Xn, s));
+  SkinnyEpi eg{};
+  eg.h = h->dHf; eg.ldh = dff;
+  HIPCHK(launch_skinny<E>(SK_SWIGLU, Xn, reinterpret_cast<const E*>(w.wgu), 2 * dff, d, S, eg, s));
+  HIPCHK(launch_skinny<E>(SK_RESID, reinterpret_cast<const E*>(h->dHf), reinterpret_cast<const E*>(w.wd), d, dff, S, er, s));
+  return MOR_OK;
+}
+
+template <typename E>
+mor_status dec_iteration(mor_handle_s* h, hipStream_t s) {
+  const int n_s = h->n_s;
+  HIPCHK(launch_dec_schedule(h->dec, s));
+  mor_status st = dec_layer<E>(h, h->blk[0], DL_FIRST, 0, s);
+  if (st != MOR_OK) return st;
+  HIPCHK(launch_dec_prep(h->dec, s));
+  for (int j = 1; j <= n_s; ++j) {
+    st = dec_layer<E>(h, h->blk[j], DL_SHARED, j, s);
+    if (st != MOR_OK) return st;
+  }
+  HIPCHK(launch_dec_update(h->dec, s));
+  st = dec_layer<E>(h, h->blk[n_s + 1], DL_LAST, 0, s);
+  if (st != MOR_OK) return st;
+  HIPCHK(launch_dec_output(h->dec, s));
+  return MOR_OK;
+}
+
 template <typename T>
 mor_status copy_block(mor_handle_s* h, const mor_block_weights& src, const BlockPacked& dst,
                       hipStream_t s) {
@@ -449,6 +561,15 @@ mor_status mor_init(const mor_config* cfg, const mor_weights* w, void* workspace
   // Cache slots past a sequence's active count are read (and masked) by the attention tiles;
   // zeroing the cache once keeps them finite.
   if (e == hipSuccess) e = hipMemsetAsync(h->kv, 0, h->kv_half_bytes * 2 * h->nstreams, s);
+  if (e == hipSuccess && h->decode) {
+    const int d = cfg->d_model;
+    e = hipMemsetAsync(h->dXn, 0, 64 * (size_t)d * h->es, s);
+    if (e == hipSuccess) e = hipMemsetAsync(h->dQkv, 0, 64 * (size_t)h->nqkv * 4, s);
+    if (e == hipSuccess) e = hipMemsetAsync(h->dO, 0, 64 * (size_t)h->nq * h->es, s);
+    if (e == hipSuccess) e = hipMemsetAsync(h->dHf, 0, 64 * (size_t)cfg->d_ff * h->es, s);
+    if (e == hipSuccess) e = hipMemsetAsync(h->dec.glob, 0, G_COUNT * 4, s);
+    if (e == hipSuccess) e = hipMemsetAsync(h->dec.sl_req, 0xFF, cfg->max_slots * 4, s);
+  }
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     delete h;
@@ -512,6 +633,60 @@ mor_status mor_get_error_flags(mor_handle* h, void* stream, uint32_t* flags) {
   HIPCHK(hipStreamSynchronize(s));
   HIPCHK(hipMemsetAsync(h->err, 0, 4, s));
   HIPCHK(hipStreamSynchronize(s));
+  return MOR_OK;
+}
+
+mor_status mor_decode_submit(mor_handle* h, int32_t n_req, const int32_t* lengths,
+                             const float* inputs, float* outputs, int8_t* exit_depth,
+                             float* h_dump, float* z_dump, void* stream) {
+  if (!h) return fail(MOR_E_INVALID, "null handle");
+  if (!h->decode) return fail(MOR_E_STATE, "handle was planned without decode state (max_slots = 0)");
+  if (n_req < 1 || !lengths || !inputs || !outputs || !exit_depth)
+    return fail(MOR_E_INVALID, "n_req < 1 or null pointer");
+  const mor_config& c = h->cfg;
+  if (n_req > c.max_requests) return fail(MOR_E_SHAPE, "n_req > max_requests");
+  std::vector<int32_t> off(n_req);
+  long long total = 0;
+  for (int i = 0; i < n_req; ++i) {
+    if (lengths[i] < 1 || lengths[i] > c.max_seq) return fail(MOR_E_SHAPE, "request length outside 1..max_seq");
+    off[i] = (int32_t)total;
+    total += lengths[i];
+  }
+  if (total > INT32_MAX / 2) return fail(MOR_E_SHAPE, "too many tokens in one submission");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  DecArgs& a = h->dec;
+  a.inputs = inputs; a.outputs = outputs;
+  a.exit_depth = reinterpret_cast<signed char*>(exit_depth);
+  a.h_dump = h_dump; a.z_dump = z_dump;
+  HIPCHK(hipMemcpyAsync(h->dreq_len, lengths, (size_t)n_req * 4, hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemcpyAsync(h->dreq_off, off.data(), (size_t)n_req * 4, hipMemcpyHostToDevice, s));
+  if (z_dump) HIPCHK(launch_fill_f32(z_dump, (size_t)total * c.n_rec, NAN, s));
+  HIPCHK(launch_dec_reset(a, n_req, s));
+  HIPCHK(hipStreamSynchronize(s));   // the host copies above read pageable memory
+  h->submitted = true;
+  return MOR_OK;
+}
+
+mor_status mor_decode_step(mor_handle* h, int32_t n_iters, void* stream, int32_t* progress) {
+  if (!h) return fail(MOR_E_INVALID, "null handle");
+  if (!h->decode || !h->submitted) return fail(MOR_E_STATE, "no decode submission on this handle");
+  if (n_iters < 0) return fail(MOR_E_INVALID, "n_iters < 0");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (int i = 0; i < n_iters; ++i) {
+    const mor_status st = h->cfg.dtype == MOR_BF16 ? dec_iteration<bf16>(h, s) : dec_iteration<float>(h, s);
+    if (st != MOR_OK) return st;
+  }
+  if (progress) {
+    int32_t g[G_COUNT];
+    uint32_t flags = 0;
+    HIPCHK(hipMemcpyAsync(g, h->dec.glob, sizeof(g), hipMemcpyDeviceToHost, s));
+    HIPCHK(hipMemcpyAsync(&flags, h->err, 4, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+    progress[0] = g[G_TOKENS];
+    progress[1] = g[G_REQS];
+    progress[2] = g[G_ITER];
+    if (flags & ERR_KV_FULL) return fail(MOR_E_KV_FULL, "decode KV page pool exhausted");
+  }
   return MOR_OK;
 }
 

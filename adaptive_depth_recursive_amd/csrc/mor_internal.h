@@ -75,3 +75,77 @@ template <typename T>
 hipError_t launch_pack_gate_up(const T* wg, const T* wu, T* out, int dff, int d, hipStream_t s);
 
 }  // namespace mor
+
+// ------------------------------------------------------------------ depth-wise batched decode
+namespace mor {
+
+// Indices of the engine's global counters (DecArgs::glob).
+enum { G_NEXT = 0, G_TOP = 1, G_TOKENS = 2, G_REQS = 3, G_HALT = 4, G_NREQ = 5, G_ITER = 6, G_COUNT = 16 };
+// Error flag bits (shared with prefill's bit 0 = NaN router logit).
+enum { ERR_NAN_LOGIT = 1u, ERR_KV_FULL = 2u };
+// Layer kinds of one decode iteration: which slots take part and which cache stream they use.
+enum { DL_FIRST = 0, DL_SHARED = 1, DL_LAST = 2 };
+
+// Everything the decode kernels read or write. Slots are the rows of every decode GEMM (at most
+// 64, padded to 64 rows); a slot holds one request, and at most one of its tokens is in flight.
+struct DecArgs {
+  int S, R, n_s, P, pps, LS;           // slots, N_r, shared layers, page tokens, pages per stream, layer streams
+  int d, hd, hkv, hq, nq, nkv, nqkv;
+  int kv_share, unit_gate;
+  long long page_elems;                // elements of one page: K then V, each [hkv][P][hd]
+  int kv_pages;
+  // slot table
+  int* sl_req;                         // request in the slot, -1 = free
+  int* sl_pos;                         // position of the token in flight
+  int* sl_depth;                       // recursion the token runs this iteration (0 = token finished)
+  int* sl_first;                       // token admitted this iteration (runs the first layer)
+  int* sl_part;                        // slot runs the shared block this iteration
+  int* sl_exit;                        // token leaves after this iteration's recursion (runs the last layer)
+  int* sl_cnt;                         // [S][R] tokens of the request that completed recursion r
+  int* ptab;                           // [S][LS][pps] page of (slot, layer stream, page index)
+  int* free_pages;                     // [kv_pages] stack of free pages
+  int* glob;                           // [G_COUNT]
+  unsigned* err;
+  const int* req_len;                  // [n_req]
+  const int* req_off;                  // [n_req] first row of the request in inputs/outputs
+  const float* inputs;                 // [tokens][d]
+  float* outputs;                      // [tokens][d]
+  signed char* exit_depth;             // [tokens]
+  float* h_dump;                       // [tokens][R+1][d] or null
+  float* z_dump;                       // [tokens][R] or null
+  float* X;                            // [64][d] working rows
+  float* Hs;                           // [64][d] state of each slot at the start of its recursion
+  float* gate;                         // [64]
+  const float* router_w;               // [R][d]
+  const float* router_b;               // [R]
+  const float* rope_cos;               // [max_seq][hd/2]
+  const float* rope_sin;
+  void* pool;                          // KV pages
+  const float* qkv;                    // [64][nqkv] fp32 projections (before RoPE)
+  void* o;                             // [64][nq] attention output
+  float scale_log2;
+};
+
+hipError_t launch_dec_schedule(const DecArgs& a, hipStream_t s);
+template <typename T>
+hipError_t launch_dec_norm(const DecArgs& a, bool gather_inputs, const float* g, float eps, T* Xn,
+                           hipStream_t s);
+hipError_t launch_dec_prep(const DecArgs& a, hipStream_t s);
+hipError_t launch_dec_update(const DecArgs& a, hipStream_t s);
+hipError_t launch_dec_output(const DecArgs& a, hipStream_t s);
+template <typename T>
+hipError_t launch_dec_attn(const DecArgs& a, int kind, int j, hipStream_t s);
+hipError_t launch_dec_reset(const DecArgs& a, int n_req, hipStream_t s);
+
+// Skinny projections of the decode batch: out^T = W . A^T for the 64 slot rows of A.
+enum { SK_STORE = 0, SK_RESID = 1, SK_SWIGLU = 2 };
+struct SkinnyEpi {
+  float* out; int ldo;                 // SK_STORE: fp32 [64][ldo]
+  float* x; int ldx;                   // SK_RESID: fp32 residual rows
+  void* h; int ldh;                    // SK_SWIGLU: SiLU(gate) * up in the element type
+};
+template <typename T>
+hipError_t launch_skinny(int epi, const T* A, const T* W, int N, int K, int M, const SkinnyEpi& ep,
+                         hipStream_t s);
+
+}  // namespace mor

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define MOR_ABI_VERSION 1
+#define MOR_ABI_VERSION 2
 #define MOR_MAX_REC 8
 #define MOR_MAX_SHARED 64
 
@@ -80,7 +80,14 @@ typedef struct {
   int32_t dtype;                 /* mor_dtype     */
   float rms_eps;                 /* RMSNorm epsilon (1e-5)      */
   float rope_theta;              /* RoPE base (10000)            */
-  int32_t max_batch, max_seq;    /* prefill bounds the workspace is planned for */
+  int32_t max_batch, max_seq;    /* prefill bounds the workspace is planned for; max_seq also bounds
+                                    decode positions */
+  /* Depth-wise batched decode (reading notes section 4). max_slots = 0 plans no decode state. */
+  int32_t max_slots;             /* concurrent sequences, 0..64 (needs THRESHOLD routing)          */
+  int32_t kv_page_tokens;        /* tokens per KV page: 16, 32, 64 or 128                           */
+  int32_t kv_pages;              /* pages in the pool; 0 = enough for max_slots sequences of max_seq
+                                    tokens that all run every recursion                             */
+  int32_t max_requests;          /* requests one mor_decode_submit may queue                       */
 } mor_config;
 
 /* One Llama decoder layer. All device pointers. [out][in] matrices in the config dtype:
@@ -104,7 +111,8 @@ int32_t mor_abi_version(void);
 const char* mor_last_error(void);
 
 /* Bytes of device workspace mor_init needs for this config (packed weights, activations for
- * max_batch x max_seq tokens, the per-recursion KV caches, routing state). 0 if cfg is invalid. */
+ * max_batch x max_seq tokens, the per-recursion KV caches, routing state, and, with max_slots > 0,
+ * the decode engine and its KV page pool). 0 if cfg is invalid. */
 size_t mor_workspace_bytes(const mor_config* cfg);
 
 /* Validate cfg, plan the workspace, copy/pack the weights into it and upload the RoPE table
@@ -165,6 +173,46 @@ mor_status mor_get_error_flags(mor_handle* h, void* stream, uint32_t* flags);
  * the number of recorded launches, and clears the record. */
 mor_status mor_timing_enable(mor_handle* h, int32_t kind, int32_t max_launches);
 mor_status mor_timing_read(mor_handle* h, double* total_ms, int32_t* launches);
+
+/* ---------------------------------------------------------------- depth-wise batched decode
+ * Continuous depth-wise batching (reading notes section 4) of the threshold-routed model (reading
+ * notes 2.1: at inference a token continues to recursion r >= 2 iff theta_r . H + b_r > 0, i.e.
+ * sigmoid > 0.5; recursion 1 always runs). Up to max_slots requests are in flight, one token each.
+ * Every decode iteration advances every occupied slot by one recursion: a token that enters runs
+ * the first layer, all occupied slots run the n_s shared layers at their own recursion (one launch
+ * per operation for all depths), and a token whose next logit is not positive, or that finished
+ * recursion N_r, runs the last layer and writes its output. The slot then takes the request's next
+ * token at the next iteration (one token per request in flight keeps the autoregressive order), or,
+ * when the request is finished, the next queued request (FIFO, lowest free slot first).
+ * The KV caches are paged per (request, layer stream): the first layer, the last layer, and each
+ * shared layer at each recursion (recursion-wise caching, MoR paper A.3), or at recursion 1 only
+ * under SHARE_FIRST (recursions >= 2 then read the recursion-1 pages). Pages are taken from a
+ * device free list when a stream's token count reaches a page boundary and returned when the
+ * request finishes. Results of a token do not depend on which other requests share the batch.
+ *
+ * mor_decode_submit resets the engine and queues n_req requests (discarding unfinished work).
+ *   lengths    host int32 [n_req], each 1..max_seq; request i's tokens occupy rows
+ *              off_i .. off_i + len_i - 1 of the token arrays, off_i = sum of earlier lengths.
+ *   inputs     device fp32 [sum len][d]  input hidden state of every token.
+ *   outputs    device fp32 [sum len][d]  hidden state after the last layer (no norm, no LM head).
+ *   exit_depth device int8 [sum len]     recursions the token ran (1..N_r).
+ *   h_dump     device fp32 [sum len][N_r + 1][d] or NULL: H after the first layer and after each
+ *              recursion the token ran (other rows untouched).
+ *   z_dump     device fp32 [sum len][N_r] or NULL: router logit z^r (bias included) for every
+ *              recursion whose gate or exit test was evaluated; the rest is set to NaN.
+ * The buffers must stay valid until the requests are finished.
+ * Errors: MOR_E_STATE (handle planned without decode), MOR_E_INVALID, MOR_E_SHAPE (n_req >
+ * max_requests, a length outside 1..max_seq), MOR_E_HIP. */
+mor_status mor_decode_submit(mor_handle* h, int32_t n_req, const int32_t* lengths,
+                             const float* inputs, float* outputs, int8_t* exit_depth,
+                             float* h_dump, float* z_dump, void* stream);
+
+/* Enqueues n_iters decode iterations on `stream` (no host synchronisation). If progress is not
+ * NULL it then synchronises and writes {tokens finished, requests finished, iterations run} of
+ * the current submission into progress[0..2].
+ * MOR_E_KV_FULL: the page pool ran out; the engine stopped at that iteration (its tokens are
+ * not finished) and stays stopped until the next submit. Checked only when progress is given. */
+mor_status mor_decode_step(mor_handle* h, int32_t n_iters, void* stream, int32_t* progress);
 
 /* Frees the host-side handle. The workspace stays the caller's. NULL is ignored. */
 void mor_destroy(mor_handle* h);

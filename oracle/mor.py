@@ -42,6 +42,7 @@ __all__ = [
     "bf16_round", "layer_map", "recursion_of_layer", "capacity_counts", "rmsnorm",
     "rope", "attention", "block", "router_logits_fp32", "sigmoid", "select_topk",
     "prefill", "threshold_forward", "decode_sequence", "kv_entries", "to_f64_weights",
+    "calibrate_threshold_bias",
 ]
 
 
@@ -445,6 +446,37 @@ def decode_sequence(cfg, weights, inputs: np.ndarray, gate_mode: Optional[str] =
         cache["last"] = append(cache["last"], kv)
         outs[p] = o[0]
     return {"out": outs, "depth": depth, "cache": cache}
+
+
+def calibrate_threshold_bias(cfg, weights, H: np.ndarray) -> np.ndarray:
+    """Router biases b_r under which the static-threshold router keeps the configured capacities.
+
+    The pages' inference router continues a token to recursion r iff sigmoid(theta_r . H + b_r)
+    exceeds 0.5 ([Notes] 2.1), with a router trained so that the kept fractions follow the
+    capacities (3/3, 2/3, 1/3 of the sequence at N_r = 3; [Kun]). Without trained weights the
+    bias stands in for that training: b_1 = 0 (recursion 1 runs every token), and for r >= 2,
+    with b_2..b_{r-1} already fixed, b_r is minus the (1 - cap_r/cap_{r-1}) quantile of the
+    unbiased logits theta_r . H^{r-1} over the tokens active at r-1 of the calibration batch
+    H [B, T, d], so that a fraction cap_r/cap_{r-1} of them continue.
+    Returns float32 [N_r].
+    """
+    assert cfg.routing == "threshold"
+    R = cfg.n_rec
+    b = np.zeros(R, np.float32)
+    for r in range(2, R + 1):
+        trial = dict(weights)
+        bb = b.copy()
+        bb[r - 1:] = np.float32(1e30)          # keep every token open from recursion r on
+        trial["router_b"] = bb
+        res = prefill(cfg.replace(seq=H.shape[1]), trial, H)
+        zs = []
+        for p in res["per_seq"]:
+            active = p["sel"][r - 2]
+            zs.append(router_logits_fp32(p["hist"][r - 1][active], weights["router_w"][r - 1]))
+        z = np.concatenate(zs).astype(np.float64)
+        q = cfg.cap_num[r - 1] / cfg.cap_num[r - 2]
+        b[r - 1] = np.float32(-np.quantile(z, 1.0 - q))
+    return b
 
 
 def kv_entries(kv: dict, n_shared: int) -> Tuple[int, int]:

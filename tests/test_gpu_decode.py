@@ -1,0 +1,234 @@
+"""GPU parity of the depth-wise batched decode engine against the CPU oracle (needs an MI355X).
+
+The engine decodes requests token by token with the static-threshold router, many requests at
+different recursion depths sharing every launch. Its results are compared per request with the
+oracle's one-shot threshold forward of the whole request (which the oracle's own pins tie to its
+token-by-token decode with per-recursion caches):
+  - router logits bit-exact given the engine's own hidden states (stage-wise), and each exit
+    depth exactly the one those logits decide;
+  - fp32 runs free: exit depths equal the oracle's own, hidden states within 1e-4;
+  - bf16 is teacher-forced (the oracle adopts the engine's depths), hidden states within 2e-2;
+  - per-token results do not depend on the batch: 1, 2 or 5 slots give identical bits.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workload
+from tests.gpu_common import rel_err, say, tolerance
+
+pytestmark = pytest.mark.gpu
+
+BIAS_SMALL = np.array([0.0, 0.1, 0.0, -0.1], np.float32)
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _setup(cfg, slots, bias=BIAS_SMALL, kv_pages=0, page=16, n_req=None, lengths=None):
+    import adaptive_depth_recursive_amd as mor
+    W = workload.make_weights(cfg)
+    W["router_b"] = np.asarray(bias, np.float32)
+    lens = workload.make_decode_lengths(cfg, n=n_req) if lengths is None else np.asarray(lengths, np.int32)
+    say(f"[gpu] decode init {cfg.name} dtype={cfg.dtype} slots={slots} page={page} "
+        f"kv_pages={kv_pages} requests={len(lens)} tokens={int(lens.sum())}")
+    model = mor.Mor(cfg, W, max_batch=1, max_seq=cfg.max_len, max_slots=slots,
+                    kv_page_tokens=page, kv_pages=kv_pages, max_requests=len(lens))
+    return model, W, lens
+
+
+def _run(model, cfg, lens, inputs, dumps=True):
+    import torch
+    x = torch.from_numpy(np.concatenate(inputs).astype(np.float32)).cuda()
+    n = x.shape[0]
+    out = torch.zeros_like(x)
+    dep = torch.zeros(n, dtype=torch.int8, device="cuda")
+    hd = torch.full((n, cfg.n_rec + 1, cfg.d_model), np.nan, device="cuda") if dumps else None
+    zd = torch.empty((n, cfg.n_rec), device="cuda") if dumps else None
+    model.decode_submit(lens, x, out, dep, hd, zd)
+    say(f"[gpu] decode run {n} tokens")
+    iters = model.decode_run(n, chunk=16, max_iters=n * cfg.n_rec + 1000)
+    done = model.decode_step(0, sync=True)
+    torch.cuda.synchronize()
+    assert done[0] == n and done[1] == len(lens), f"unfinished: {done}"
+    res = {"out": out.cpu().numpy(), "depth": dep.cpu().numpy().astype(np.int32), "iters": iters}
+    if dumps:
+        res["h"] = hd.cpu().numpy()
+        res["z"] = zd.cpu().numpy()
+    return res
+
+
+def _offsets(lens):
+    return np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+
+
+def _check_routing(cfg, W, res, lens):
+    """Logits bit-exact given the engine's hidden states; depths exactly what they decide."""
+    R = cfg.n_rec
+    for i, (o, n) in enumerate(zip(_offsets(lens), lens)):
+        for t in range(o, o + n):
+            D = res["depth"][t]
+            assert 1 <= D <= R
+            for r in range(1, min(D + 1, R) + 1):
+                z = oracle.router_logits_fp32(res["h"][t, r - 1], W["router_w"][r - 1],
+                                              W["router_b"][r - 1])[0]
+                assert res["z"][t, r - 1].view(np.uint32) == z.view(np.uint32), (i, t, r)
+            for r in range(2, D + 1):
+                assert res["z"][t, r - 1] > 0, (t, r)
+            if D < R:
+                assert not res["z"][t, D] > 0, (t, D)
+            assert np.all(np.isnan(res["z"][t, D + 1:])), t
+
+
+def _compare(cfg, W, res, lens, inputs, teacher, which=None):
+    worst = 0.0
+    R = cfg.n_rec
+    for i, (o, n) in enumerate(zip(_offsets(lens), lens)):
+        if which is not None and i not in which:
+            continue
+        depth = res["depth"][o:o + n]
+        forced = [[np.nonzero(depth >= r)[0]] for r in range(1, R + 1)] if teacher else None
+        ref = oracle.prefill(cfg.replace(seq=int(n)), W, inputs[i][None], forced_sel=forced)
+        p = ref["per_seq"][0]
+        own = np.zeros(n, np.int32)
+        for r, sel in enumerate(p["own_sel"], start=1):
+            own[sel] = r
+        if not teacher:
+            assert np.array_equal(own, depth), f"request {i}: exit depths differ"
+        e = rel_err(res["out"][o:o + n], ref["out"][0])
+        for r in range(R + 1):
+            rows = np.nonzero(depth >= r)[0] if r else np.arange(n)
+            er = rel_err(res["h"][o + rows, r], p["hist"][r][rows])
+            assert er <= tolerance(cfg), f"request {i}: H after recursion {r} rel err {er}"
+        worst = max(worst, e)
+        assert e <= tolerance(cfg), f"request {i}: output rel err {e}"
+    return worst
+
+
+def test_decode_small_f32_free_running():
+    cfg = workload.get_config("small_thr_bf16", dtype="f32")
+    model, W, lens = _setup(cfg, slots=5)
+    inputs = workload.make_decode_inputs(cfg, lens)
+    res = _run(model, cfg, lens, inputs)
+    _check_routing(cfg, W, res, lens)
+    worst = _compare(cfg, W, res, lens, inputs, teacher=False)
+    say(f"[gpu] decode f32: {len(lens)} requests, {res['iters']} iterations, worst rel err {worst:.2e}, "
+        f"depth histogram {np.bincount(res['depth'], minlength=cfg.n_rec + 1)[1:]}")
+    model.close()
+
+
+def test_decode_small_bf16_teacher_forced():
+    cfg = workload.get_config("small_thr_bf16")
+    model, W, lens = _setup(cfg, slots=5)
+    inputs = workload.make_decode_inputs(cfg, lens)
+    res = _run(model, cfg, lens, inputs)
+    _check_routing(cfg, W, res, lens)
+    worst = _compare(cfg, W, res, lens, inputs, teacher=True)
+    say(f"[gpu] decode bf16: worst rel err {worst:.2e}")
+    model.close()
+
+
+def test_decode_small_bf16_kv_share():
+    cfg = workload.get_config("small_thr_bf16", kv_mode="share")
+    model, W, lens = _setup(cfg, slots=4)
+    inputs = workload.make_decode_inputs(cfg, lens)
+    res = _run(model, cfg, lens, inputs)
+    _check_routing(cfg, W, res, lens)
+    _compare(cfg, W, res, lens, inputs, teacher=True)
+    model.close()
+
+
+def test_decode_f32_kv_share_free_running():
+    cfg = workload.get_config("small_thr_bf16", dtype="f32", kv_mode="share")
+    model, W, lens = _setup(cfg, slots=3, page=32)
+    inputs = workload.make_decode_inputs(cfg, lens)
+    res = _run(model, cfg, lens, inputs)
+    _check_routing(cfg, W, res, lens)
+    _compare(cfg, W, res, lens, inputs, teacher=False)
+    model.close()
+
+
+def test_decode_results_independent_of_batch():
+    """Depth-wise batching changes only which tokens share a launch, never a token's result:
+    1, 2 and 5 slots (different admission orders, page sizes and batch mixes) give identical bits."""
+    cfg = workload.get_config("small_thr_bf16")
+    outs = []
+    for slots, page in ((5, 16), (2, 32), (1, 64)):
+        model, W, lens = _setup(cfg, slots=slots, page=page)
+        inputs = workload.make_decode_inputs(cfg, lens)
+        res = _run(model, cfg, lens, inputs, dumps=False)
+        outs.append(res)
+        model.close()
+    for r in outs[1:]:
+        assert np.array_equal(r["depth"], outs[0]["depth"])
+        assert np.array_equal(r["out"].view(np.uint32), outs[0]["out"].view(np.uint32))
+
+
+def test_decode_unit_gate_all_depths():
+    """Biases that open every recursion: every token runs N_r recursions (the fixed-depth
+    recursive model, token by token)."""
+    cfg = workload.get_config("small_thr_bf16", dtype="f32", gate_mode="unit")
+    model, W, lens = _setup(cfg, slots=4, bias=[0.0, 50.0, 50.0, 50.0], n_req=5)
+    inputs = workload.make_decode_inputs(cfg, lens)
+    res = _run(model, cfg, lens, inputs)
+    assert np.all(res["depth"] == cfg.n_rec)
+    _compare(cfg, W, res, lens, inputs, teacher=False)
+    model.close()
+
+
+def test_decode_single_token_requests_and_resubmit():
+    """Length-1 requests (admit and leave every few iterations), then a second submission on
+    the same handle starts from a clean engine."""
+    cfg = workload.get_config("small_thr_bf16", dtype="f32")
+    model, W, _ = _setup(cfg, slots=3, lengths=[1] * 7)
+    for lens in ([1] * 7, [5, 1, 3]):
+        lens = np.array(lens, np.int32)
+        inputs = workload.make_decode_inputs(cfg, lens)
+        res = _run(model, cfg, lens, inputs)
+        _compare(cfg, W, res, lens, inputs, teacher=False)
+    model.close()
+
+
+def test_decode_kv_pool_exhaustion_reported():
+    """A pool too small for the batch: the engine stops at the iteration that needs a page it
+    cannot get, reports MOR_E_KV_FULL, and every kernel still runs to completion."""
+    import torch
+    import adaptive_depth_recursive_amd as mor
+    cfg = workload.get_config("small_thr_bf16")
+    model, W, lens = _setup(cfg, slots=5, kv_pages=12, page=16)
+    inputs = workload.make_decode_inputs(cfg, lens)
+    x = torch.from_numpy(np.concatenate(inputs)).cuda()
+    out = torch.zeros_like(x)
+    dep = torch.zeros(x.shape[0], dtype=torch.int8, device="cuda")
+    model.decode_submit(lens, x, out, dep)
+    with pytest.raises(mor.MorError) as e:
+        for _ in range(200):
+            model.decode_step(8, sync=True)
+    assert e.value.status == mor.MOR_E_KV_FULL
+    torch.cuda.synchronize()
+    model.close()
+
+
+def test_decode_full_size_sampled():
+    """The 360M-shape MoR-4 decode workload at its launch configuration (51 slots, 64-token
+    pages): the first 80 requests of the seeded length distribution, routing checked stage-wise
+    on every token, two requests checked against the oracle (teacher-forced)."""
+    cfg = workload.get_config("smol360m_mor4_decode")
+    bias = np.array(_gold("decode_router_bias.json")["router_b"], np.float32)
+    lens = np.minimum(workload.make_decode_lengths(cfg)[:80], 300)
+    model, W, lens = _setup(cfg, slots=cfg.slots, bias=bias, page=64, lengths=lens)
+    inputs = workload.make_decode_inputs(cfg, lens)
+    res = _run(model, cfg, lens, inputs)
+    _check_routing(cfg, W, res, lens)
+    short = [int(i) for i in np.argsort(lens)[:2]]
+    say(f"[cpu] oracle on requests {short} (lengths {lens[short]})")
+    worst = _compare(cfg, W, res, lens, inputs, teacher=True, which=set(short))
+    say(f"[gpu] full-size decode: {int(lens.sum())} tokens, {res['iters']} iterations, "
+        f"depths {np.bincount(res['depth'], minlength=cfg.n_rec + 1)[1:]}, worst rel err {worst:.2e}")
+    model.close()

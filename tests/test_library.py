@@ -31,7 +31,7 @@ def test_header_symbols_exported():
 
 def test_abi_version():
     mor = _lib()
-    assert mor.lib().mor_abi_version() == 1
+    assert mor.lib().mor_abi_version() == 2
 
 
 @pytest.mark.parametrize("name", sorted(workload.CONFIGS))
@@ -88,3 +88,37 @@ def test_null_handle_calls_rejected():
     assert L.mor_prefill(None, None, 1, 1, None, None, None, None, None, None) == mor.MOR_E_INVALID
     assert L.mor_route(None, None, None, None, 1, 1, 1, None, None, None, None) == mor.MOR_E_INVALID
     L.mor_destroy(None)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("max_slots", 65), ("kv_page_tokens", 48), ("routing", 0), ("max_requests", 0), ("kv_pages", -1)])
+def test_invalid_decode_configs_rejected(field, value):
+    mor = _lib()
+    c = mor.make_config(workload.get_config("small_thr_bf16"), max_slots=5, kv_page_tokens=16,
+                        max_requests=4)
+    assert mor.lib().mor_workspace_bytes(ctypes.byref(c)) > 0
+    setattr(c, field, value)
+    assert mor.lib().mor_workspace_bytes(ctypes.byref(c)) == 0
+    assert mor.lib().mor_last_error()
+
+
+def test_decode_workspace_includes_page_pool():
+    """The default pool holds max_slots requests of max_seq tokens at full depth: pages of one
+    layer's K and V (2 x Hkv x P x hd elements) for the 2 unique and N_r x n_s shared layer streams."""
+    mor = _lib()
+    cfg = workload.get_config("smol360m_mor4_decode")
+    base = mor.workspace_bytes(mor.make_config(cfg, max_batch=1))
+    c = mor.make_config(cfg, max_batch=1, max_slots=51, kv_page_tokens=64, max_requests=1024)
+    full = mor.workspace_bytes(c)
+    page_bytes = 2 * 5 * 64 * 64 * 2
+    pages = 51 * (2 + 4 * 7) * (2048 // 64)
+    assert pages * page_bytes < full - base < pages * page_bytes + 64 * 2 ** 20
+    c.kv_pages = 100
+    assert mor.workspace_bytes(c) < base + 100 * page_bytes + 64 * 2 ** 20
+
+
+def test_decode_calls_rejected_without_handle():
+    mor = _lib()
+    L = mor.lib()
+    assert L.mor_decode_submit(None, 1, None, None, None, None, None, None, None) == mor.MOR_E_INVALID
+    assert L.mor_decode_step(None, 1, None, None) == mor.MOR_E_INVALID

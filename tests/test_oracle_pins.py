@@ -370,3 +370,22 @@ def test_threshold_recursion_one_always_runs():
     x = workload.make_decode_inputs(cfg, np.array([9]))[0]
     one = oracle.threshold_forward(cfg, W, x)
     assert np.all(one["depth"] == 1)
+
+
+def test_threshold_bias_calibration_reproduces_capacities():
+    """The bias calibration that stands in for a trained threshold router: on its own
+    calibration batch the realised pass fractions are cap_r / cap_{r-1} (3/4, 2/3, 1/2 for
+    MoR-4) up to the quantile's one-token granularity, and recursion 1 keeps every token."""
+    cfg = workload.get_config("small_thr_bf16", dtype="f32")
+    W = workload.make_weights(cfg)
+    H = workload.make_calibration_inputs(cfg, 3, 64)
+    b = oracle.calibrate_threshold_bias(cfg, W, H)
+    assert b.dtype == np.float32 and b[0] == 0.0
+    W["router_b"] = b
+    res = oracle.prefill(cfg.replace(seq=64), W, H)
+    n = [sum(len(p["sel"][r]) for p in res["per_seq"]) for r in range(cfg.n_rec)]
+    assert n[0] == 3 * 64
+    for r in range(1, cfg.n_rec):
+        frac = n[r] / n[r - 1]
+        want = cfg.cap_num[r] / cfg.cap_num[r - 1]
+        assert abs(frac - want) <= 1.0 / n[r - 1] + 1e-12, (r, frac, want)
