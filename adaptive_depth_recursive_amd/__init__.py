@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.mor_decode_submit.argtypes = [vp, i32, ctypes.POINTER(i32), vp, vp, vp, vp, vp, vp]
         L.mor_decode_step.restype = i32
         L.mor_decode_step.argtypes = [vp, i32, vp, ctypes.POINTER(i32)]
+        L.mor_decode_stats.restype = i32
+        L.mor_decode_stats.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int64)]
         L.mor_destroy.restype = None
         L.mor_destroy.argtypes = [vp]
         _lib = L
@@ -99,7 +101,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("mor_abi_version", "mor_last_error", "mor_workspace_bytes", "mor_init",
             "mor_prefill", "mor_route", "mor_kv_view", "mor_get_error_flags", "mor_timing_enable",
-            "mor_timing_read", "mor_decode_submit", "mor_decode_step", "mor_destroy")
+            "mor_timing_read", "mor_decode_submit", "mor_decode_step", "mor_decode_stats", "mor_destroy")
 KERNEL_KINDS = {"qkv": 1, "attention": 2, "o_proj": 3, "gate_up": 4, "down": 5}
 
 
@@ -293,6 +295,14 @@ class Mor:
         prog = (ctypes.c_int32 * 3)()
         _check(lib().mor_decode_step(self.handle, n_iters, _stream(stream), prog))
         return prog[0], prog[1], prog[2]
+
+    def decode_stats(self, stream=None) -> Dict[str, int]:
+        """mor_decode_stats as a dict (synchronises)."""
+        out = (ctypes.c_int64 * 8)()
+        _check(lib().mor_decode_stats(self.handle, _stream(stream), out))
+        keys = ("tokens", "requests", "admitted", "iterations", "weight_bytes", "kv_read_bytes",
+                "kv_write_bytes", "act_bytes")
+        return dict(zip(keys, (int(v) for v in out)))
 
     def decode_run(self, total_tokens: int, chunk: int = 32, max_iters: int = 1 << 22, stream=None):
         """Steps until every submitted token is finished; returns the iterations run."""

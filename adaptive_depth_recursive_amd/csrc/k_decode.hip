@@ -140,7 +140,39 @@ __global__ __launch_bounds__(64) void k_dec_schedule(DecArgs a) {
     a.sl_part[s] = (!full && part) ? 1 : 0;
     a.sl_exit[s] = 0;
   }
+  // algorithmic bytes of this iteration's first layer and shared block (the last layer's are
+  // counted by k_dec_output once the exits are known)
+  const long long kvtok = 2LL * a.hkv * a.hd * a.es;        // K and V of one token in one layer
+  long long kv_rd = 0, kv_wr = 0, act = 0;
+  int n_first = 0, n_part = 0;
+  if (!full && part) {
+    const int idx = a.sl_cnt[s * a.R + r - 1];
+    if (admit) { kv_rd += (long long)pos * kvtok; kv_wr += kvtok; act += 4LL * a.d; n_first = 1; }
+    if (a.kv_share && r >= 2) {
+      kv_rd += (long long)a.n_s * (a.sl_cnt[s * a.R] ) * kvtok;
+    } else {
+      kv_rd += (long long)a.n_s * idx * kvtok;
+      kv_wr += (long long)a.n_s * kvtok;
+    }
+    n_part = 1;
+  }
+  int tot_first, tot_part;
+  (void)wave_scan_excl(n_first, &tot_first);
+  (void)wave_scan_excl(n_part, &tot_part);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kv_rd += __shfl_xor(kv_rd, o);
+    kv_wr += __shfl_xor(kv_wr, o);
+    act += __shfl_xor(act, o);
+  }
   if (s == 0) {
+    if (a.stats) {
+      const long long wb = a.layer_weight_bytes * ((tot_first ? 1 : 0) + (tot_part ? a.n_s : 0));
+      a.stats[ST_WEIGHT] += (unsigned long long)wb;
+      a.stats[ST_KV_READ] += (unsigned long long)kv_rd;
+      a.stats[ST_KV_WRITE] += (unsigned long long)kv_wr;
+      a.stats[ST_ACT] += (unsigned long long)act;
+    }
     g[G_NEXT] = next + taken;
     g[G_ITER] += 1;
     if (full) {
@@ -170,6 +202,7 @@ __global__ void k_dec_reset(DecArgs a, int n_req) {
   if (i < 64) a.gate[i] = 0.f;
   if (i < 64 * a.d) { a.X[i] = 0.f; a.Hs[i] = 0.f; }
   if (i < G_COUNT) a.glob[i] = (i == G_TOP) ? a.kv_pages : (i == G_NREQ) ? n_req : 0;
+  if (a.stats && i < ST_COUNT) a.stats[i] = 0;
 }
 
 hipError_t launch_dec_reset(const DecArgs& a, int n_req, hipStream_t s) {
@@ -318,6 +351,26 @@ hipError_t launch_dec_update(const DecArgs& a, hipStream_t s) {
 __global__ __launch_bounds__(256) void k_dec_output(DecArgs a) {
   const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = lane_id();
+  if (a.stats && blockIdx.x == 0 && threadIdx.x < 64) {
+    // last-layer bytes of this iteration (every slot's exit flag is still set here)
+    const int t = threadIdx.x;
+    const long long kvtok = 2LL * a.hkv * a.hd * a.es;
+    const bool ex = t < a.S && a.sl_exit[t];
+    long long rd = ex ? (long long)a.sl_pos[t] * kvtok : 0;
+    int n = ex ? 1 : 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      rd += __shfl_xor(rd, o);
+      n += __shfl_xor(n, o);
+    }
+    if (t == 0 && n) {
+      a.stats[ST_WEIGHT] += (unsigned long long)a.layer_weight_bytes;
+      a.stats[ST_KV_READ] += (unsigned long long)rd;
+      a.stats[ST_KV_WRITE] += (unsigned long long)(n * kvtok);
+      a.stats[ST_ACT] += (unsigned long long)(n * 4LL * a.d);
+    }
+  }
+  __syncthreads();
   if (s >= a.S || !a.sl_exit[s]) return;
   const int d = a.d;
   const int tok = a.req_off[a.sl_req[s]] + a.sl_pos[s];
@@ -325,8 +378,7 @@ __global__ __launch_bounds__(256) void k_dec_output(DecArgs a) {
   float4* o = reinterpret_cast<float4*>(a.outputs + (size_t)tok * d);
   for (int c = lane; c < d / 4; c += WAVE) o[c] = x[c];
   if (lane == 0) {
-    a.sl_depth[s] = 0;
-    a.sl_exit[s] = 0;
+    a.sl_depth[s] = 0;                     // the exit flag is cleared by the next schedule
     atomicAdd(&a.glob[G_TOKENS], 1);
     if (a.sl_pos[s] + 1 == a.req_len[a.sl_req[s]]) atomicAdd(&a.glob[G_REQS], 1);
   }

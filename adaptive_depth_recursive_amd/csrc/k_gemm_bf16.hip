@@ -13,6 +13,7 @@
 //  - two LDS stages: the loads of step k+1 are in flight while step k is multiplied;
 //  - workgroups are renumbered so that the ones sharing an activation tile land on one XCD
 //    (the hardware deals workgroups round-robin over the 8 XCDs, each with its own L2).
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -53,21 +54,29 @@ __device__ __forceinline__ bf16x8 frag(const char* base, int row, int chunk) {
 template <int BN, int BM, int EPI>
 __global__ __launch_bounds__(256, 1) void k_gemm_bf16(const bf16* __restrict__ A,
                                                       const bf16* __restrict__ W, int N, int K,
-                                                      int tiles_n, const int* __restrict__ meta,
-                                                      GemmEpi ep) {
+                                                      int tiles_n, int group_m,
+                                                      const int* __restrict__ meta, GemmEpi ep) {
   constexpr int WN = BN / 2, WM = BM / 2;
   constexpr int FN = WN / 16, FM = WM / 16;
   constexpr int STAGE = (BN + BM) * kRowBytes;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int M = meta[0];
-  // XCD-aware renumbering: blocks b, b+8, b+16, ... run on one XCD; give them consecutive tiles.
+  // XCD-aware renumbering: blocks b, b+8, b+16, ... run on one XCD; give them consecutive
+  // positions of the tile order.
   const int nblk = gridDim.x;
   const int bid = blockIdx.x;
   const int per_xcd = nblk / 8, rem = nblk % 8;
   const int xcd = bid % 8, slot = bid / 8;
-  const int tile = (xcd < rem ? xcd * (per_xcd + 1) : rem * (per_xcd + 1) + (xcd - rem) * per_xcd) + slot;
-  const int tm = tile / tiles_n, tn = tile % tiles_n;
+  const int t = (xcd < rem ? xcd * (per_xcd + 1) : rem * (per_xcd + 1) + (xcd - rem) * per_xcd) + slot;
+  // Tile order: groups of group_m activation row-blocks, swept one weight column-block at a
+  // time with the row-blocks fastest, so the workgroups resident on an XCD share a few
+  // activation slabs and a few weight slabs in its L2.
+  const int tiles_m = nblk / tiles_n;
+  const int gsz = group_m * tiles_n;
+  const int grp = t / gsz, gi = t - grp * gsz;
+  const int rows_g = min(group_m, tiles_m - grp * group_m);
+  const int tm = grp * group_m + gi % rows_g, tn = gi / rows_g;
   const int m0 = tm * BM, n0 = tn * BN;
   if (m0 >= M) return;
 
@@ -194,6 +203,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(const bf16* __restrict__ A
 namespace {
 
 int g_forced_tile = -1;   // tuning override from MOR_GEMM_TILE ("256x256", "256x128", "128x128")
+int g_group_m = -1;       // tuning override of the tile-order group (MOR_GEMM_GROUP_M)
+
+int group_m() {
+  if (g_group_m == -1) {
+    g_group_m = 8;
+    if (const char* s = getenv("MOR_GEMM_GROUP_M")) g_group_m = std::max(1, atoi(s));
+  }
+  return g_group_m;
+}
 
 int forced_tile() {
   if (g_forced_tile == -1) {
@@ -213,10 +231,11 @@ hipError_t launch_cfg(int epi, const bf16* A, const bf16* W, int N, int K, int m
   const int tn = (N + BN - 1) / BN, tm = (m_upper + BM - 1) / BM;
   const int nblk = tn * tm;
   if (nblk == 0) return hipSuccess;
+  const int gm = group_m();
   switch (epi) {
-    case EPI_QKV: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_QKV>), dim3(nblk), dim3(256), 0, s, A, W, N, K, tn, meta, ep); break;
-    case EPI_RESID: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_RESID>), dim3(nblk), dim3(256), 0, s, A, W, N, K, tn, meta, ep); break;
-    default: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_SWIGLU>), dim3(nblk), dim3(256), 0, s, A, W, N, K, tn, meta, ep); break;
+    case EPI_QKV: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_QKV>), dim3(nblk), dim3(256), 0, s, A, W, N, K, tn, gm, meta, ep); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_RESID>), dim3(nblk), dim3(256), 0, s, A, W, N, K, tn, gm, meta, ep); break;
+    default: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_SWIGLU>), dim3(nblk), dim3(256), 0, s, A, W, N, K, tn, gm, meta, ep); break;
   }
   return hipGetLastError();
 }

@@ -213,6 +213,7 @@ size_t plan(const mor_config& c, mor_handle_s* h, char* base) {
     da.ptab = cur.take<int>((size_t)S * LS * pps * 4);
     da.free_pages = cur.take<int>((size_t)kv_pages * 4);
     da.glob = cur.take<int>(G_COUNT * 4);
+    da.stats = cur.take<unsigned long long>(ST_COUNT * 8);
     dreq_len = cur.take<int>((size_t)c.max_requests * 4);
     dreq_off = cur.take<int>((size_t)c.max_requests * 4);
     da.X = cur.take<float>(64 * d * 4);
@@ -252,6 +253,8 @@ size_t plan(const mor_config& c, mor_handle_s* h, char* base) {
       da.rope_cos = rope_cos; da.rope_sin = rope_sin;
       da.qkv = dQkv; da.o = dO;
       da.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
+      da.es = (int)es;
+      da.layer_weight_bytes = (long long)((nqkv * d + d * nq + 2 * dff * d + d * dff) * es);
       h->dec = da;
     }
   }
@@ -687,6 +690,20 @@ mor_status mor_decode_step(mor_handle* h, int32_t n_iters, void* stream, int32_t
     progress[2] = g[G_ITER];
     if (flags & ERR_KV_FULL) return fail(MOR_E_KV_FULL, "decode KV page pool exhausted");
   }
+  return MOR_OK;
+}
+
+mor_status mor_decode_stats(mor_handle* h, void* stream, int64_t* out) {
+  if (!h || !out) return fail(MOR_E_INVALID, "null pointer");
+  if (!h->decode) return fail(MOR_E_STATE, "handle was planned without decode state (max_slots = 0)");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int32_t g[G_COUNT];
+  unsigned long long st[ST_COUNT];
+  HIPCHK(hipMemcpyAsync(g, h->dec.glob, sizeof(g), hipMemcpyDeviceToHost, s));
+  HIPCHK(hipMemcpyAsync(st, h->dec.stats, sizeof(st), hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  out[0] = g[G_TOKENS]; out[1] = g[G_REQS]; out[2] = g[G_NEXT]; out[3] = g[G_ITER];
+  for (int i = 0; i < ST_COUNT; ++i) out[4 + i] = (int64_t)st[i];
   return MOR_OK;
 }
 

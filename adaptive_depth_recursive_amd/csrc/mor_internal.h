@@ -124,7 +124,13 @@ struct DecArgs {
   const float* qkv;                    // [64][nqkv] fp32 projections (before RoPE)
   void* o;                             // [64][nq] attention output
   float scale_log2;
+  // algorithmic bytes of the iterations (measurement): weights of every layer that runs, K/V
+  // read and appended by the participating slots, input and output rows
+  unsigned long long* stats;           // [ST_COUNT]
+  long long layer_weight_bytes;
+  int es;                              // bytes per element of the weights and the cache
 };
+enum { ST_WEIGHT = 0, ST_KV_READ = 1, ST_KV_WRITE = 2, ST_ACT = 3, ST_COUNT = 4 };
 
 hipError_t launch_dec_schedule(const DecArgs& a, hipStream_t s);
 template <typename T>

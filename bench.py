@@ -110,6 +110,65 @@ def cpu_baseline(cfg, weights, H0_np, seq_len: int):
                       f"oracle in float64 with bf16 storage points; {dt:.1f} s"}
 
 
+def decode_bench(args):
+    """Depth-wise batched MoR-4 decode of the 360M-shape model (51 slots, 1024 requests with
+    Geometric(mean 256) lengths, threshold exit with the calibrated router biases). Timed over
+    the steady-state window: iterations while the request queue is not empty (every slot busy)."""
+    import numpy as np
+    import torch
+    import adaptive_depth_recursive_amd as mor
+    import workload
+
+    cfg = workload.get_config("smol360m_mor4_decode")
+    W = workload.make_weights(cfg)
+    with open(os.path.join(ROOT, "tests", "golden", "decode_router_bias.json")) as f:
+        W["router_b"] = np.array(json.load(f)["router_b"], np.float32)
+    lens = workload.make_decode_lengths(cfg)
+    x = torch.from_numpy(np.concatenate(workload.make_decode_inputs(cfg, lens))).cuda()
+    out = torch.empty_like(x)
+    dep = torch.zeros(x.shape[0], dtype=torch.int8, device="cuda")
+    model = mor.Mor(cfg, W, max_batch=1, max_seq=cfg.max_len, max_slots=cfg.slots,
+                    kv_page_tokens=args.kv_page_tokens, max_requests=len(lens))
+    model.decode_submit(lens, x, out, dep)
+    model.decode_step(args.decode_warmup)          # slots fill on the first iteration
+    st0 = model.decode_stats()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ms, last, chunks = 0.0, st0, 0
+    while last["iterations"] - st0["iterations"] < args.decode_iters:
+        ev[0].record()
+        model.decode_step(args.decode_chunk)
+        ev[1].record()
+        st = model.decode_stats()
+        if st["admitted"] >= len(lens):          # queue drained during this chunk: window ends
+            break
+        ms += ev[0].elapsed_time(ev[1])
+        last, chunks = st, chunks + 1
+    it = last["iterations"] - st0["iterations"]
+    tok = last["tokens"] - st0["tokens"]
+    byt = sum(last[k] - st0[k] for k in ("weight_bytes", "kv_read_bytes", "kv_write_bytes", "act_bytes"))
+    kvr = last["kv_read_bytes"] - st0["kv_read_bytes"]
+    s_ = ms / 1e3
+    done = dep[dep > 0].cpu().numpy()
+    model.close()
+    return {
+        "metric": "MoR-4 decode tokens/sec (360M-shape, 51 slots, depth-wise batching, bf16)",
+        "value": tok / s_ if s_ else None, "unit": "tokens/s",
+        "ms_per_iteration": ms / max(it, 1), "tokens_per_iteration": tok / max(it, 1),
+        "window": f"{it} iterations ({chunks} chunks of {args.decode_chunk}) while the queue of "
+                  f"{len(lens)} requests was not empty, after {args.decode_warmup} warmup iterations",
+        "roofline": {"bound": "hbm", "achieved": byt / s_ / 1e9 if s_ else None, "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": byt / s_ / PEAK_HBM if s_ else None, "traffic": None,
+                     "algorithmic_bytes_per_iteration": byt / max(it, 1),
+                     "kv_read_bytes_per_iteration": kvr / max(it, 1)},
+        "exit_depth_histogram": np.bincount(done, minlength=cfg.n_rec + 1)[1:].tolist(),
+        "config": {"workload": f"{cfg.name}: d {cfg.d_model}, {cfg.n_q_heads}/{cfg.n_kv_heads} heads x "
+                               f"{cfg.head_dim}, FFN {cfg.d_ff}, L {cfg.n_layers} (N_r {cfg.n_rec} x "
+                               f"{cfg.n_shared} shared), threshold exit, {cfg.slots} slots, "
+                               f"{len(lens)} requests, {int(lens.sum())} tokens, "
+                               f"{args.kv_page_tokens}-token KV pages"},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +178,12 @@ def main():
     ap.add_argument("--roofline-kernel", default="gate_up", choices=sorted(KERNEL_SOURCES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seq", type=int, default=2048, help="tokens of the CPU-baseline sample")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--decode-only", action="store_true")
+    ap.add_argument("--decode-iters", type=int, default=3000, help="cap of the timed decode window")
+    ap.add_argument("--decode-chunk", type=int, default=64)
+    ap.add_argument("--decode-warmup", type=int, default=64)
+    ap.add_argument("--kv-page-tokens", type=int, default=64)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -142,6 +207,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4}))
+        return
+
+    if args.decode_only:
+        print(json.dumps(decode_bench(args)), flush=True)
         return
 
     cfg = workload.get_config(args.config)
@@ -215,6 +284,9 @@ def main():
     model.close()
     del h, h_out
     torch.cuda.empty_cache()
+    if not args.no_decode:
+        result["decode"] = decode_bench(args)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, W, H0, args.cpu_seq)
     print(json.dumps(result), flush=True)

@@ -214,6 +214,13 @@ mor_status mor_decode_submit(mor_handle* h, int32_t n_req, const int32_t* length
  * not finished) and stays stopped until the next submit. Checked only when progress is given. */
 mor_status mor_decode_step(mor_handle* h, int32_t n_iters, void* stream, int32_t* progress);
 
+/* Synchronises `stream` and reports the current submission (measurement):
+ *   out[0] tokens finished, out[1] requests finished, out[2] requests admitted from the queue,
+ *   out[3] iterations run, then the algorithmic bytes of those iterations: out[4] weights (every
+ *   layer that ran for at least one token, once per iteration), out[5] K/V read from the cache,
+ *   out[6] K/V appended, out[7] input and output rows. */
+mor_status mor_decode_stats(mor_handle* h, void* stream, int64_t* out);
+
 /* Frees the host-side handle. The workspace stays the caller's. NULL is ignored. */
 void mor_destroy(mor_handle* h);
 
