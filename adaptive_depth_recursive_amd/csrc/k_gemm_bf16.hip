@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(const bf16* __restrict__ A
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float gt = acc[i][j][e], up = acc[i + 1][j][e];
-          o[e] = gt / (1.f + __expf(-gt)) * up;
+          o[e] = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
         }
         Vec4<bf16>::store(reinterpret_cast<bf16*>(ep.h) + (size_t)m * ep.ldh + (np >> 1) + g4,
                           o[0], o[1], o[2], o[3]);
