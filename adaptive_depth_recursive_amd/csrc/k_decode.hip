@@ -212,126 +212,175 @@ hipError_t launch_dec_reset(const DecArgs& a, int n_req, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ RMSNorm of the slot rows
-// One wave per slot row. With gather_inputs (first layer), admitted slots first load their
-// token's input hidden state into X, and every other row of X is cleared.
+// One 256-thread workgroup per slot row (thread t owns the float4 chunks t, t+256, ...). With
+// gather_inputs (first layer), admitted slots first load their token's input hidden state into
+// X, and every other row of X is cleared; with fold > 0 the residual projection's partial sums
+// are first added into X (split order).
+constexpr int ROW_THREADS = 256, ROW_CHUNKS = 4;   // rows up to 4096 elements
+
+__device__ __forceinline__ float block_sum_fixed(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void k_dec_norm(DecArgs a, int gather, const float* __restrict__ g,
-                                                  float eps, T* __restrict__ Xn) {
-  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = lane_id();
-  if (s >= a.S) return;
-  const int d = a.d;
+__global__ __launch_bounds__(ROW_THREADS) void k_dec_norm(DecArgs a, int gather, int fold,
+                                                          const float* __restrict__ g, float eps,
+                                                          T* __restrict__ Xn) {
+  __shared__ float red[4];
+  const int s = blockIdx.x, t = threadIdx.x;
+  const int d = a.d, nc = d / 4;
   float4* x = reinterpret_cast<float4*>(a.X + (size_t)s * d);
-  if (gather) {
-    if (a.sl_first[s]) {
-      const int tok = a.req_off[a.sl_req[s]] + a.sl_pos[s];
-      const float4* src = reinterpret_cast<const float4*>(a.inputs + (size_t)tok * d);
-      for (int c = lane; c < d / 4; c += WAVE) x[c] = src[c];
-    } else {
-      for (int c = lane; c < d / 4; c += WAVE) x[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const bool load_in = gather && a.sl_first[s];
+  const float4* src = load_in ? reinterpret_cast<const float4*>(
+                                    a.inputs + (size_t)(a.req_off[a.sl_req[s]] + a.sl_pos[s]) * d)
+                              : nullptr;
+  float4 v[ROW_CHUNKS];
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < ROW_CHUNKS; ++u) {
+    const int c = t + u * ROW_THREADS;
+    float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < nc) {
+      if (gather) {
+        if (load_in) w = src[c];
+      } else {
+        w = x[c];
+        for (int k = 0; k < fold; ++k) {
+          const float4 pv = reinterpret_cast<const float4*>(a.px + ((size_t)k * 64 + s) * d)[c];
+          w.x += pv.x; w.y += pv.y; w.z += pv.z; w.w += pv.w;
+        }
+      }
+      if (gather || fold) x[c] = w;
+    }
+    v[u] = w;
+    ss += w.x * w.x + w.y * w.y + w.z * w.z + w.w * w.w;
+  }
+  ss = block_sum_fixed(ss, red);
+  const float rinv = 1.f / sqrtf(ss / (float)d + eps);
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  T* out = Xn + (size_t)s * d;
+#pragma unroll
+  for (int u = 0; u < ROW_CHUNKS; ++u) {
+    const int c = t + u * ROW_THREADS;
+    if (c < nc) {
+      const float4 gg = g4[c];
+      Vec4<T>::store(out + 4 * c, v[u].x * rinv * gg.x, v[u].y * rinv * gg.y, v[u].z * rinv * gg.z,
+                     v[u].w * rinv * gg.w);
     }
   }
-  const float4* g4 = reinterpret_cast<const float4*>(g);
-  float ss = 0.f;
-  for (int c = lane; c < d / 4; c += WAVE) {
-    const float4 v = x[c];
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  ss = wave_sum(ss);
-  const float rinv = 1.f / sqrtf(ss / (float)d + eps);
-  T* out = Xn + (size_t)s * d;
-  for (int c = lane; c < d / 4; c += WAVE) {
-    const float4 v = x[c], gg = g4[c];
-    Vec4<T>::store(out + 4 * c, v.x * rinv * gg.x, v.y * rinv * gg.y, v.z * rinv * gg.z,
-                   v.w * rinv * gg.w);
-  }
 }
 
 template <typename T>
-hipError_t launch_dec_norm(const DecArgs& a, bool gather_inputs, const float* g, float eps, T* Xn,
-                           hipStream_t s) {
-  hipLaunchKernelGGL((k_dec_norm<T>), dim3((a.S + 3) / 4), dim3(256), 0, s, a, gather_inputs ? 1 : 0,
-                     g, eps, Xn);
+hipError_t launch_dec_norm(const DecArgs& a, bool gather_inputs, int fold, const float* g,
+                           float eps, T* Xn, hipStream_t s) {
+  if (a.d > 4 * ROW_CHUNKS * ROW_THREADS) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_dec_norm<T>), dim3(a.S), dim3(ROW_THREADS), 0, s, a, gather_inputs ? 1 : 0,
+                     fold, g, eps, Xn);
   return hipGetLastError();
 }
-template hipError_t launch_dec_norm<float>(const DecArgs&, bool, const float*, float, float*, hipStream_t);
-template hipError_t launch_dec_norm<bf16>(const DecArgs&, bool, const float*, float, bf16*, hipStream_t);
+template hipError_t launch_dec_norm<float>(const DecArgs&, bool, int, const float*, float, float*, hipStream_t);
+template hipError_t launch_dec_norm<bf16>(const DecArgs&, bool, int, const float*, float, bf16*, hipStream_t);
 
 // ------------------------------------------------------------------ recursion entry / exit
-// Fixed-order router logit of a row (the order of k_router): returns the value in every lane.
-__device__ __forceinline__ float dec_logit(const float* __restrict__ h, const float* __restrict__ w,
-                                           const float* bias, int d, int lane) {
+// Router logit of a row in the fixed order of k_router (lane l of 64 sums the products of
+// elements l, l+64, ... in ascending order, product and sum rounded separately, then the pairwise
+// fold): the products are formed by the whole workgroup into LDS, wave 0 runs the 64 chains.
+__device__ __forceinline__ float row_logit_fixed(const float* prod, int d, float bias) {
+  const int lane = threadIdx.x & 63;
   float p = 0.f;
-  for (int i = lane; i < d; i += WAVE) p = add_rn(p, mul_rn(h[i], w[i]));
+  for (int i = lane; i < d; i += WAVE) p = add_rn(p, prod[i]);
   p = fold_fixed(p);
-  if (bias) p = add_rn(p, bias[0]);
+  p = add_rn(p, bias);
   return (p == 0.f) ? 0.f : p;
 }
 
+constexpr int ROW_MAX = 4 * ROW_CHUNKS * ROW_THREADS;
+
 // Start of the recursion of every occupied slot: a newly admitted token's state is the first
-// layer's output, a continuing token's state is carried in Hs; the shared block works on X.
-// The gate of the recursion is sigmoid(theta_r . H + b_r).
-__global__ __launch_bounds__(256) void k_dec_prep(DecArgs a) {
-  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = lane_id();
-  if (s >= a.S || !a.sl_part[s]) return;
+// layer's output (plus its down projection's partial sums), a continuing token's state is
+// carried in Hs; the shared block works on X. The gate of the recursion is
+// sigmoid(theta_r . H + b_r).
+__global__ __launch_bounds__(ROW_THREADS) void k_dec_prep(DecArgs a, int fold) {
+  __shared__ float prod[ROW_MAX];
+  const int s = blockIdx.x, t = threadIdx.x;
+  if (!a.sl_part[s]) return;
   const int d = a.d, r = a.sl_depth[s];
-  float* x = a.X + (size_t)s * d;
-  float* hs = a.Hs + (size_t)s * d;
+  float* __restrict__ x = a.X + (size_t)s * d;
+  float* __restrict__ hs = a.Hs + (size_t)s * d;
+  const float* __restrict__ w = a.router_w + (size_t)(r - 1) * d;
   const int tok = a.req_off[a.sl_req[s]] + a.sl_pos[s];
-  if (a.sl_first[s]) {
-    for (int c = lane; c < d; c += WAVE) hs[c] = x[c];
-    if (a.h_dump)
-      for (int c = lane; c < d; c += WAVE) a.h_dump[((size_t)tok * (a.R + 1)) * d + c] = x[c];
-  } else {
-    for (int c = lane; c < d; c += WAVE) x[c] = hs[c];
+  const bool first = a.sl_first[s];
+  float* __restrict__ dump = (first && a.h_dump) ? a.h_dump + ((size_t)tok * (a.R + 1)) * d : nullptr;
+  for (int c = t; c < d; c += ROW_THREADS) {
+    float h;
+    if (first) {
+      h = x[c];
+      for (int k = 0; k < fold; ++k) h += a.px[((size_t)k * 64 + s) * d + c];
+      hs[c] = h;                           // the folded first-layer output is the state...
+    } else {
+      h = hs[c];
+    }
+    x[c] = h;                              // ...and the shared block's input
+    if (dump) dump[c] = h;
+    prod[c] = mul_rn(h, w[c]);
   }
-  const float z = dec_logit(hs, a.router_w + (size_t)(r - 1) * d, a.router_b + (r - 1), d, lane);
-  if (lane == 0) {
+  __syncthreads();
+  if (t >= WAVE) return;
+  const float z = row_logit_fixed(prod, d, a.router_b[r - 1]);
+  if (t == 0) {
     if (z != z) atomicOr(a.err, (unsigned)ERR_NAN_LOGIT);
     a.gate[s] = a.unit_gate ? -1.f : 1.f / (1.f + __expf(-z));
     if (a.z_dump) a.z_dump[(size_t)tok * a.R + (r - 1)] = z;
   }
 }
 
-hipError_t launch_dec_prep(const DecArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_dec_prep, dim3((a.S + 3) / 4), dim3(256), 0, s, a);
+hipError_t launch_dec_prep(const DecArgs& a, int fold, hipStream_t s) {
+  if (a.d > ROW_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_dec_prep, dim3(a.S), dim3(ROW_THREADS), 0, s, a, fold);
   return hipGetLastError();
 }
 
-// End of the recursion: H <- H + g (F(H) - H) (or F(H) under unit gating), then the exit test on
-// the next router logit: the token continues iff r < N_r and theta_{r+1} . H + b_{r+1} > 0.
-__global__ __launch_bounds__(256) void k_dec_update(DecArgs a) {
-  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = lane_id();
-  if (s >= a.S || !a.sl_part[s]) return;
+// End of the recursion: F(H) = X + the last shared layer's down-projection partial sums;
+// H <- H + g (F(H) - H) (or F(H) under unit gating), then the exit test on the next router
+// logit: the token continues iff r < N_r and theta_{r+1} . H + b_{r+1} > 0.
+__global__ __launch_bounds__(ROW_THREADS) void k_dec_update(DecArgs a, int fold) {
+  __shared__ float prod[ROW_MAX];
+  const int s = blockIdx.x, t = threadIdx.x;
+  if (!a.sl_part[s]) return;
   const int d = a.d, r = a.sl_depth[s];
   const float g = a.gate[s];
-  float* x = a.X + (size_t)s * d;
-  float* hs = a.Hs + (size_t)s * d;
+  float* __restrict__ x = a.X + (size_t)s * d;
+  float* __restrict__ hs = a.Hs + (size_t)s * d;
   const int tok = a.req_off[a.sl_req[s]] + a.sl_pos[s];
-  const float* w = (r < a.R) ? a.router_w + (size_t)r * d : nullptr;
-  float p = 0.f;
-  for (int c = lane; c < d; c += WAVE) {
-    const float hv = hs[c], xv = x[c];
+  const float* __restrict__ w = (r < a.R) ? a.router_w + (size_t)r * d : nullptr;
+  float* __restrict__ dump = a.h_dump ? a.h_dump + ((size_t)tok * (a.R + 1) + r) * d : nullptr;
+  for (int c = t; c < d; c += ROW_THREADS) {
+    float xv = x[c];
+    for (int k = 0; k < fold; ++k) xv += a.px[((size_t)k * 64 + s) * d + c];
+    const float hv = hs[c];
     const float hn = (g < 0.f) ? xv : hv + g * (xv - hv);
     hs[c] = hn;
     x[c] = hn;
-    if (a.h_dump) a.h_dump[((size_t)tok * (a.R + 1) + r) * d + c] = hn;
-    if (w) p = add_rn(p, mul_rn(hn, w[c]));
+    if (dump) dump[c] = hn;
+    if (w) prod[c] = mul_rn(hn, w[c]);
   }
+  __syncthreads();
+  if (t >= WAVE) return;
   bool leave = true;
   if (w) {
-    p = fold_fixed(p);
-    p = add_rn(p, a.router_b[r]);
-    p = (p == 0.f) ? 0.f : p;
+    const float p = row_logit_fixed(prod, d, a.router_b[r]);
     leave = !(p > 0.f);
-    if (lane == 0) {
+    if (t == 0) {
       if (p != p) atomicOr(a.err, (unsigned)ERR_NAN_LOGIT);
       if (a.z_dump) a.z_dump[(size_t)tok * a.R + r] = p;
     }
   }
-  if (lane == 0) {
+  if (t == 0) {
     a.sl_cnt[s * a.R + r - 1] += 1;
     if (leave) {
       a.sl_exit[s] = 1;
@@ -342,18 +391,18 @@ __global__ __launch_bounds__(256) void k_dec_update(DecArgs a) {
   }
 }
 
-hipError_t launch_dec_update(const DecArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_dec_update, dim3((a.S + 3) / 4), dim3(256), 0, s, a);
+hipError_t launch_dec_update(const DecArgs& a, int fold, hipStream_t s) {
+  if (a.d > ROW_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_dec_update, dim3(a.S), dim3(ROW_THREADS), 0, s, a, fold);
   return hipGetLastError();
 }
 
-// Tokens that ran the last layer: write the output row, mark the token finished.
-__global__ __launch_bounds__(256) void k_dec_output(DecArgs a) {
-  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = lane_id();
-  if (a.stats && blockIdx.x == 0 && threadIdx.x < 64) {
+// Tokens that ran the last layer: output = X + the last layer's down-projection partial sums;
+// mark the token finished. Workgroup 0 also counts the last layer's algorithmic bytes.
+__global__ __launch_bounds__(ROW_THREADS) void k_dec_output(DecArgs a, int fold) {
+  const int s = blockIdx.x, t = threadIdx.x;
+  if (a.stats && s == 0 && t < 64) {
     // last-layer bytes of this iteration (every slot's exit flag is still set here)
-    const int t = threadIdx.x;
     const long long kvtok = 2LL * a.hkv * a.hd * a.es;
     const bool ex = t < a.S && a.sl_exit[t];
     long long rd = ex ? (long long)a.sl_pos[t] * kvtok : 0;
@@ -371,40 +420,53 @@ __global__ __launch_bounds__(256) void k_dec_output(DecArgs a) {
     }
   }
   __syncthreads();
-  if (s >= a.S || !a.sl_exit[s]) return;
+  if (!a.sl_exit[s]) return;
   const int d = a.d;
   const int tok = a.req_off[a.sl_req[s]] + a.sl_pos[s];
   const float4* x = reinterpret_cast<const float4*>(a.X + (size_t)s * d);
   float4* o = reinterpret_cast<float4*>(a.outputs + (size_t)tok * d);
-  for (int c = lane; c < d / 4; c += WAVE) o[c] = x[c];
-  if (lane == 0) {
+  for (int c = t; c < d / 4; c += ROW_THREADS) {
+    float4 v = x[c];
+    for (int k = 0; k < fold; ++k) {
+      const float4 pv = reinterpret_cast<const float4*>(a.px + ((size_t)k * 64 + s) * d)[c];
+      v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
+    }
+    o[c] = v;
+  }
+  if (t == 0) {
     a.sl_depth[s] = 0;                     // the exit flag is cleared by the next schedule
     atomicAdd(&a.glob[G_TOKENS], 1);
     if (a.sl_pos[s] + 1 == a.req_len[a.sl_req[s]]) atomicAdd(&a.glob[G_REQS], 1);
   }
 }
 
-hipError_t launch_dec_output(const DecArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_dec_output, dim3((a.S + 3) / 4), dim3(256), 0, s, a);
+hipError_t launch_dec_output(const DecArgs& a, int fold, hipStream_t s) {
+  hipLaunchKernelGGL(k_dec_output, dim3(a.S), dim3(ROW_THREADS), 0, s, a, fold);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ decode attention
-// One workgroup per (slot, KV head). It rotates the slot's new query heads and key (RoPE at the
-// token's position, fp32, then rounded to the element type), appends the new K/V to the slot's
-// page of the layer stream, and attends over the cached keys of that stream plus the new one:
-// recursion-wise caching reads the stream of the token's own recursion; recursive KV sharing at
-// r >= 2 appends nothing and reads the recursion-1 stream of the same shared layer.
-// Waves take 64-key tiles in turn (lane = key for the scores, lane = head-dim element for PV)
-// and are merged in wave order at the end.
+// One workgroup of 8 waves per (slot, KV head). It rotates the slot's new query heads and key
+// (RoPE at the token's position, fp32, then rounded to the element type), appends the new K/V to
+// the slot's page of the layer stream, and attends over the cached keys of that stream plus the
+// new one: recursion-wise caching reads the stream of the token's own recursion; recursive KV
+// sharing at r >= 2 appends nothing and reads the recursion-1 stream of the same shared layer.
+// Waves take 64-key tiles in turn. Scores: lane = key (its K row against the G query heads held
+// in LDS). Values: the tile's V rows are copied into LDS with 16-byte loads, then lane = head-dim
+// element accumulates over the tile's keys. The waves' partial results are merged in wave order.
+constexpr int DA_WAVES = 8;
+
 template <typename T, int HD, int G>
-__global__ __launch_bounds__(256) void k_dec_attn(DecArgs a, int kind, int j) {
+__global__ __launch_bounds__(DA_WAVES * 64) void k_dec_attn(DecArgs a, int kind, int j) {
   constexpr int KT = 64;
+  constexpr int CH = 16 / (int)sizeof(T);            // elements per 16-byte chunk
+  constexpr int RCHUNKS = HD / CH;                   // chunks per K/V row
   __shared__ float sq[G][HD];
   __shared__ float skn[HD], svn[HD];
-  __shared__ float sp[4][G][KT];
-  __shared__ float sm[4][G], sl[4][G];
-  __shared__ float sacc[4][G][HD];
+  __shared__ float sp[DA_WAVES][G][KT];
+  __shared__ __attribute__((aligned(16))) T sv[DA_WAVES][KT * HD];
+  __shared__ float sm[DA_WAVES][G], sl[DA_WAVES][G];
+  __shared__ float sacc[DA_WAVES][G][HD];
 
   const int s = blockIdx.x, kvh = blockIdx.y;
   if (s >= a.S) return;
@@ -429,18 +491,20 @@ __global__ __launch_bounds__(256) void k_dec_attn(DecArgs a, int kind, int j) {
   }
   const int half = HD / 2;
   const float* qkv = a.qkv + (size_t)s * a.nqkv;
-  for (int i = tid; i < (G + 2) * HD; i += 256) {
+  for (int i = tid; i < (G + 2) * HD; i += DA_WAVES * 64) {
     const int hh = i / HD, c = i % HD;
     const int pc = c < half ? c + half : c - half;
     const float* base;
     if (hh < G) base = qkv + (kvh * G + hh) * HD;
     else if (hh == G) base = qkv + a.nq + kvh * HD;
     else base = qkv + a.nq + a.nkv + kvh * HD;
-    float v = base[c];
+    const size_t split = (size_t)64 * a.nqkv;     // partial sums of the K splits, added in order
+    float v = base[c], vp = base[pc];
+    for (int k = 1; k < a.kqkv; ++k) { v += base[k * split + c]; vp += base[k * split + pc]; }
     if (hh <= G) {
       const int f = c % half;
       const float cs = a.rope_cos[pos * half + f], sn = a.rope_sin[pos * half + f];
-      v = c < half ? v * cs - base[pc] * sn : v * cs + base[pc] * sn;
+      v = c < half ? v * cs - vp * sn : v * cs + vp * sn;
     }
     v = to_f32(from_f32<T>(v));
     if (hh < G) sq[hh][c] = v;
@@ -473,7 +537,16 @@ __global__ __launch_bounds__(256) void k_dec_attn(DecArgs a, int kind, int j) {
     }
   }
   const int* pt = a.ptab + ((size_t)s * a.LS + ls_r) * a.pps;
-  for (int t0 = wave * KT; t0 < nkeys; t0 += 4 * KT) {
+  T* svw = sv[wave];
+  for (int t0 = wave * KT; t0 < nkeys; t0 += DA_WAVES * KT) {
+    const int nt = min(KT, nkeys - t0);
+    // V rows of the tile -> LDS (16-byte chunks, consecutive lanes on consecutive chunks)
+    for (int cidx = lane; cidx < nt * RCHUNKS; cidx += 64) {
+      const int kk = cidx / RCHUNKS, cc = cidx % RCHUNKS;
+      const int ik = t0 + kk;
+      const T* vr = pool + (size_t)pt[ik / a.P] * a.page_elems + vofs + ((size_t)kvh * a.P + ik % a.P) * HD;
+      *reinterpret_cast<uint4*>(svw + kk * HD + cc * CH) = *reinterpret_cast<const uint4*>(vr + cc * CH);
+    }
     const int i = t0 + lane;
     const bool valid = i < nkeys;
     float sc[G];
@@ -481,20 +554,18 @@ __global__ __launch_bounds__(256) void k_dec_attn(DecArgs a, int kind, int j) {
     for (int hh = 0; hh < G; ++hh) sc[hh] = 0.f;
     if (valid) {
       const T* kr = pool + (size_t)pt[i / a.P] * a.page_elems + ((size_t)kvh * a.P + i % a.P) * HD;
-      constexpr int CH = 16 / (int)sizeof(T);
+      union { uint4 u; T e[CH]; } kc[RCHUNKS];
 #pragma unroll
-      for (int c0 = 0; c0 < HD; c0 += CH) {
-        union { uint4 u; T e[CH]; } kc;
-        kc.u = *reinterpret_cast<const uint4*>(kr + c0);
+      for (int c0 = 0; c0 < RCHUNKS; ++c0) kc[c0].u = *reinterpret_cast<const uint4*>(kr + c0 * CH);
+#pragma unroll
+      for (int c0 = 0; c0 < RCHUNKS; ++c0)
 #pragma unroll
         for (int e = 0; e < CH; ++e) {
-          const float kv = to_f32(kc.e[e]);
+          const float kv = to_f32(kc[c0].e[e]);
 #pragma unroll
-          for (int hh = 0; hh < G; ++hh) sc[hh] += sq[hh][c0 + e] * kv;
+          for (int hh = 0; hh < G; ++hh) sc[hh] += sq[hh][c0 * CH + e] * kv;
         }
-      }
     }
-    const int nt = min(KT, nkeys - t0);
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       const float v = valid ? sc[hh] * sl2 : -INFINITY;
@@ -509,19 +580,21 @@ __global__ __launch_bounds__(256) void k_dec_attn(DecArgs a, int kind, int j) {
       m[hh] = mn;
       sp[wave][hh][lane] = to_f32(from_f32<T>(p));
     }
+    // this wave's LDS writes (probabilities, V rows) are read back by other lanes of the wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): this wave's LDS writes are done
-    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (lane_c) {
+#pragma unroll 8
       for (int kk = 0; kk < nt; ++kk) {
-        const int ik = t0 + kk;
-        const T* vr = pool + (size_t)pt[ik / a.P] * a.page_elems + vofs + ((size_t)kvh * a.P + ik % a.P) * HD;
-        const float vv = to_f32(vr[lane]);
+        const float vv = to_f32(svw[kk * HD + lane]);
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) acc[hh] += sp[wave][hh][kk] * vv;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
@@ -534,9 +607,9 @@ __global__ __launch_bounds__(256) void k_dec_attn(DecArgs a, int kind, int j) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       float M = -INFINITY;
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][hh]);
+      for (int w = 0; w < DA_WAVES; ++w) M = fmaxf(M, sm[w][hh]);
       float L = 0.f, o = 0.f;
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < DA_WAVES; ++w) {
         const float f = (sm[w][hh] == -INFINITY) ? 0.f : exp2f(sm[w][hh] - M);
         L += sl[w][hh] * f;
         o += sacc[w][hh][lane] * f;
@@ -548,12 +621,12 @@ __global__ __launch_bounds__(256) void k_dec_attn(DecArgs a, int kind, int j) {
 
 template <typename T, int HD>
 static hipError_t dec_attn_g(const DecArgs& a, int kind, int j, hipStream_t s) {
-  dim3 grid(a.S, a.hkv);
+  dim3 grid(a.S, a.hkv), block(DA_WAVES * 64);
   switch (a.hq / a.hkv) {
-    case 1: hipLaunchKernelGGL((k_dec_attn<T, HD, 1>), grid, dim3(256), 0, s, a, kind, j); break;
-    case 2: hipLaunchKernelGGL((k_dec_attn<T, HD, 2>), grid, dim3(256), 0, s, a, kind, j); break;
-    case 3: hipLaunchKernelGGL((k_dec_attn<T, HD, 3>), grid, dim3(256), 0, s, a, kind, j); break;
-    case 4: hipLaunchKernelGGL((k_dec_attn<T, HD, 4>), grid, dim3(256), 0, s, a, kind, j); break;
+    case 1: hipLaunchKernelGGL((k_dec_attn<T, HD, 1>), grid, block, 0, s, a, kind, j); break;
+    case 2: hipLaunchKernelGGL((k_dec_attn<T, HD, 2>), grid, block, 0, s, a, kind, j); break;
+    case 3: hipLaunchKernelGGL((k_dec_attn<T, HD, 3>), grid, block, 0, s, a, kind, j); break;
+    case 4: hipLaunchKernelGGL((k_dec_attn<T, HD, 4>), grid, block, 0, s, a, kind, j); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -573,27 +646,34 @@ template hipError_t launch_dec_attn<bf16>(const DecArgs&, int, int, hipStream_t)
 
 // ------------------------------------------------------------------ skinny projections
 // out^T = W . A^T for the 64 rows of A (the slots), weights on the MFMA A side. A workgroup owns
-// RG groups of 16 weight rows; its 4 waves take interleaved 128-byte slices of K, multiply all
-// 64 slot rows, and the partial sums are added in wave order in LDS (deterministic). Wave w then
+// RG groups of 16 weight rows and one contiguous range of 128-byte K slices (K is split over
+// grid.y so that enough CUs stream the weights); its 4 waves take the range's slices in turn,
+// loading the fragments of SK_BATCH of their slices before multiplying them (several loads per
+// lane in flight), and add their partial sums in wave order in LDS (deterministic). Wave w then
 // finishes slot rows 16w..16w+15: each lane holds 4 consecutive output columns of one row.
+constexpr int SK_WAVES = 4, SK_BATCH = 3;
+
 template <typename T, int RG, int EPI>
-__global__ __launch_bounds__(256) void k_skinny(const T* __restrict__ A, const T* __restrict__ W,
-                                                int N, int K, int M, SkinnyEpi ep) {
+__global__ __launch_bounds__(SK_WAVES * 64) void k_skinny(const T* __restrict__ A,
+                                                          const T* __restrict__ W, int N, int K,
+                                                          int M, SkinnyEpi ep) {
   typedef Mma<T> MM;
   constexpr int UK = 128 / (int)sizeof(T);          // K elements per slice
   constexpr int NS = UK / MM::KSTEP;               // MFMA steps per slice
-  __shared__ f32x4 red[4][RG][4][64];
+  __shared__ f32x4 red[SK_WAVES][RG][4][64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * 16 * RG;
+  const int nu = K / UK;
+  const int per = (nu + gridDim.y - 1) / gridDim.y;
+  const int ulo = blockIdx.y * per, uhi = min(nu, ulo + per);
   f32x4 acc[RG][4];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
     for (int mf = 0; mf < 4; ++mf) acc[rg][mf] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nu = K / UK;
   const T* wrow[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) wrow[rg] = W + (size_t)(n0 + 16 * rg + fr) * K + g * MM::KW;
@@ -601,22 +681,37 @@ __global__ __launch_bounds__(256) void k_skinny(const T* __restrict__ A, const T
 #pragma unroll
   for (int mf = 0; mf < 4; ++mf) arow[mf] = A + (size_t)(16 * mf + fr) * K + g * MM::KW;
 
-  for (int u = wave; u < nu; u += 4) {
-    typename MM::frag wa[RG][NS], xb[4][NS];
+  for (int u0 = ulo + wave; u0 < uhi; u0 += SK_WAVES * SK_BATCH) {
+    typename MM::frag wa[SK_BATCH][RG][NS], xb[SK_BATCH][4][NS];
 #pragma unroll
-    for (int ks = 0; ks < NS; ++ks) {
-      const int k = u * UK + ks * MM::KSTEP;
+    for (int bt = 0; bt < SK_BATCH; ++bt) {
+      const int u = min(u0 + bt * SK_WAVES, uhi - 1);  // past the range: a repeated slice, zeroed below
 #pragma unroll
-      for (int rg = 0; rg < RG; ++rg) wa[rg][ks] = MM::load(wrow[rg] + k);
+      for (int ks = 0; ks < NS; ++ks) {
+        const int k = u * UK + ks * MM::KSTEP;
 #pragma unroll
-      for (int mf = 0; mf < 4; ++mf) xb[mf][ks] = MM::load(arow[mf] + k);
+        for (int rg = 0; rg < RG; ++rg) wa[bt][rg][ks] = MM::load(wrow[rg] + k);
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) xb[bt][mf][ks] = MM::load(arow[mf] + k);
+      }
     }
+    // keep every load of the batch ahead of the multiplies (several loads in flight per lane)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < NS; ++ks)
+    for (int bt = 0; bt < SK_BATCH; ++bt) {
+      if (u0 + bt * SK_WAVES >= uhi) {             // repeated slice: multiply zeros instead
 #pragma unroll
-      for (int rg = 0; rg < RG; ++rg)
+        for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-        for (int mf = 0; mf < 4; ++mf) acc[rg][mf] = MM::mma(wa[rg][ks], xb[mf][ks], acc[rg][mf]);
+          for (int ks = 0; ks < NS; ++ks) wa[bt][rg][ks] = typename MM::frag{};
+      }
+#pragma unroll
+      for (int ks = 0; ks < NS; ++ks)
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+          for (int mf = 0; mf < 4; ++mf) acc[rg][mf] = MM::mma(wa[bt][rg][ks], xb[bt][mf][ks], acc[rg][mf]);
+    }
   }
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
@@ -629,25 +724,17 @@ __global__ __launch_bounds__(256) void k_skinny(const T* __restrict__ A, const T
   for (int rg = 0; rg < RG; ++rg) {
     v[rg] = red[0][rg][mf][lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) v[rg] += red[w][rg][mf][lane];
+    for (int w = 1; w < SK_WAVES; ++w) v[rg] += red[w][rg][mf][lane];
   }
   const int m = 16 * mf + fr;
   if (m >= M) return;
-  if constexpr (EPI == SK_STORE) {
+  if constexpr (EPI == SK_PARTIAL) {
+    float* out = ep.out + (size_t)blockIdx.y * 64 * ep.ldo;
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
       const int n = n0 + 16 * rg + 4 * g;
-      *reinterpret_cast<float4*>(ep.out + (size_t)m * ep.ldo + n) =
+      *reinterpret_cast<float4*>(out + (size_t)m * ep.ldo + n) =
           make_float4(v[rg][0], v[rg][1], v[rg][2], v[rg][3]);
-    }
-  } else if constexpr (EPI == SK_RESID) {
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-      const int n = n0 + 16 * rg + 4 * g;
-      float4* px = reinterpret_cast<float4*>(ep.x + (size_t)m * ep.ldx + n);
-      float4 x = *px;
-      x.x += v[rg][0]; x.y += v[rg][1]; x.z += v[rg][2]; x.w += v[rg][3];
-      *px = x;
     }
   } else {  // SK_SWIGLU: weight rows are gate/up groups of 16 (RG == 2)
     const int col = (n0 >> 1) + 4 * g;
@@ -655,30 +742,25 @@ __global__ __launch_bounds__(256) void k_skinny(const T* __restrict__ A, const T
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float gt = v[0][e], up = v[1][e];
-      o[e] = gt / (1.f + __expf(-gt)) * up;
+      o[e] = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
     }
     Vec4<T>::store(reinterpret_cast<T*>(ep.h) + (size_t)m * ep.ldh + col, o[0], o[1], o[2], o[3]);
   }
 }
 
 template <typename T>
-hipError_t launch_skinny(int epi, const T* A, const T* W, int N, int K, int M, const SkinnyEpi& ep,
-                         hipStream_t s) {
-  if (K % 64 || N % 32 || M > 64) return hipErrorInvalidValue;
-  switch (epi) {
-    case SK_STORE:
-      hipLaunchKernelGGL((k_skinny<T, 1, SK_STORE>), dim3(N / 16), dim3(256), 0, s, A, W, N, K, M, ep);
-      break;
-    case SK_RESID:
-      hipLaunchKernelGGL((k_skinny<T, 1, SK_RESID>), dim3(N / 16), dim3(256), 0, s, A, W, N, K, M, ep);
-      break;
-    default:
-      hipLaunchKernelGGL((k_skinny<T, 2, SK_SWIGLU>), dim3(N / 32), dim3(256), 0, s, A, W, N, K, M, ep);
-      break;
+hipError_t launch_skinny(int epi, const T* A, const T* W, int N, int K, int M, int ksplit,
+                         const SkinnyEpi& ep, hipStream_t s) {
+  if (K % 64 || N % 32 || M > 64 || ksplit < 1 || ksplit > 8) return hipErrorInvalidValue;
+  if (epi == SK_PARTIAL) {
+    hipLaunchKernelGGL((k_skinny<T, 1, SK_PARTIAL>), dim3(N / 16, ksplit), dim3(SK_WAVES * 64), 0, s, A, W, N, K, M, ep);
+  } else {
+    if (ksplit != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_skinny<T, 2, SK_SWIGLU>), dim3(N / 32, 1), dim3(SK_WAVES * 64), 0, s, A, W, N, K, M, ep);
   }
   return hipGetLastError();
 }
-template hipError_t launch_skinny<float>(int, const float*, const float*, int, int, int, const SkinnyEpi&, hipStream_t);
-template hipError_t launch_skinny<bf16>(int, const bf16*, const bf16*, int, int, int, const SkinnyEpi&, hipStream_t);
+template hipError_t launch_skinny<float>(int, const float*, const float*, int, int, int, int, const SkinnyEpi&, hipStream_t);
+template hipError_t launch_skinny<bf16>(int, const bf16*, const bf16*, int, int, int, int, const SkinnyEpi&, hipStream_t);
 
 }  // namespace mor

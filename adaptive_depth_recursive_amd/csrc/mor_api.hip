@@ -11,6 +11,7 @@
 // Expert-choice counts are static, so nothing is read back to the host during a call.
 #include <climits>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -97,10 +98,15 @@ struct mor_handle_s {
   int* dreq_len = nullptr;       // [max_requests]
   int* dreq_off = nullptr;       // [max_requests]
   void* dXn = nullptr;           // [64][d]
-  float* dQkv = nullptr;         // [64][nqkv]
+  float* dQkv = nullptr;         // [kSplitQKV][64][nqkv] partial sums
+  float* dPx = nullptr;          // [8][64][d] partial sums of the O / down projections
   void* dO = nullptr;            // [64][nq]
   void* dHf = nullptr;           // [64][d_ff]
   bool submitted = false;
+  // decode iterations replayed as a captured HIP graph (kernel arguments fixed per submission)
+  hipStream_t cap_stream = nullptr;
+  hipGraph_t dec_graph = nullptr;
+  hipGraphExec_t dec_exec = nullptr;
   // measurement: HIP events around every launch of one kernel kind
   int timing_kind = 0;
   std::vector<hipEvent_t> ev;
@@ -205,6 +211,7 @@ size_t plan(const mor_config& c, mor_handle_s* h, char* base) {
   int *dreq_len = nullptr, *dreq_off = nullptr;
   void *dXn = nullptr, *dO = nullptr, *dHf = nullptr;
   float* dQkv = nullptr;
+  float* dPx = nullptr;
   if (S) {
     da.sl_req = cur.take<int>(S * 4); da.sl_pos = cur.take<int>(S * 4);
     da.sl_depth = cur.take<int>(S * 4); da.sl_first = cur.take<int>(S * 4);
@@ -220,7 +227,8 @@ size_t plan(const mor_config& c, mor_handle_s* h, char* base) {
     da.Hs = cur.take<float>(64 * d * 4);
     da.gate = cur.take<float>(64 * 4);
     dXn = cur.take<void>(64 * d * es);
-    dQkv = cur.take<float>(64 * nqkv * 4);
+    dQkv = cur.take<float>(4 * 64 * nqkv * 4);
+    dPx = cur.take<float>(8 * 64 * d * 4);
     dO = cur.take<void>(64 * nq * es);
     dHf = cur.take<void>(64 * dff * es);
     da.pool = cur.take<void>((size_t)kv_pages * page_bytes);
@@ -239,7 +247,7 @@ size_t plan(const mor_config& c, mor_handle_s* h, char* base) {
     if (S) {
       h->kv_pages = kv_pages; h->pps = pps; h->LS = LS; h->page_bytes = page_bytes;
       h->dreq_len = dreq_len; h->dreq_off = dreq_off;
-      h->dXn = dXn; h->dQkv = dQkv; h->dO = dO; h->dHf = dHf;
+      h->dXn = dXn; h->dQkv = dQkv; h->dPx = dPx; h->dO = dO; h->dHf = dHf;
       da.S = S; da.R = R; da.n_s = n_s; da.P = P; da.pps = pps; da.LS = LS;
       da.d = (int)d; da.hd = (int)hd; da.hkv = c.n_kv_heads; da.hq = c.n_q_heads;
       da.nq = (int)nq; da.nkv = (int)nkv; da.nqkv = (int)nqkv;
@@ -251,7 +259,7 @@ size_t plan(const mor_config& c, mor_handle_s* h, char* base) {
       da.req_len = dreq_len; da.req_off = dreq_off;
       da.router_w = router_w; da.router_b = router_b;
       da.rope_cos = rope_cos; da.rope_sin = rope_sin;
-      da.qkv = dQkv; da.o = dO;
+      da.qkv = dQkv; da.kqkv = 4; da.px = dPx; da.o = dO;
       da.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
       da.es = (int)es;
       da.layer_weight_bytes = (long long)((nqkv * d + d * nq + 2 * dff * d + d * dff) * es);
@@ -445,25 +453,32 @@ mor_status prefill_impl(mor_handle_s* h, const float* h_in, int B, int T, float*
 }
 
 // ------------------------------------------------------------------ decode iteration
+// K splits of the decode projections: enough workgroups to spread the weight streaming over the
+// CUs (a projection has only N/16 column groups of 64 slot rows).
+constexpr int kSplitQKV = 4, kSplitO = 4, kSplitDown = 8;
+
+// fold_in: residual partial sums of the previous layer still to be added into X (0 if X is
+// already complete). Returns through fold_out the partial sums this layer leaves (its down
+// projection's), which the next consumer of X adds.
 template <typename E>
-mor_status dec_layer(mor_handle_s* h, const BlockPacked& w, int kind, int j, hipStream_t s) {
+mor_status dec_layer(mor_handle_s* h, const BlockPacked& w, int kind, int j, int fold_in, hipStream_t s) {
   const mor_config& c = h->cfg;
   const DecArgs& a = h->dec;
   const int d = c.d_model, dff = c.d_ff, S = a.S;
   E* Xn = reinterpret_cast<E*>(h->dXn);
-  HIPCHK(launch_dec_norm<E>(a, kind == DL_FIRST, w.g_attn, c.rms_eps, Xn, s));
+  HIPCHK(launch_dec_norm<E>(a, kind == DL_FIRST, kind == DL_FIRST ? 0 : fold_in, w.g_attn, c.rms_eps, Xn, s));
   SkinnyEpi eq{};
   eq.out = h->dQkv; eq.ldo = h->nqkv;
-  HIPCHK(launch_skinny<E>(SK_STORE, Xn, reinterpret_cast<const E*>(w.wqkv), h->nqkv, d, S, eq, s));
+  HIPCHK(launch_skinny<E>(SK_PARTIAL, Xn, reinterpret_cast<const E*>(w.wqkv), h->nqkv, d, S, kSplitQKV, eq, s));
   HIPCHK(launch_dec_attn<E>(a, kind, j, s));
-  SkinnyEpi er{};
-  er.x = a.X; er.ldx = d;
-  HIPCHK(launch_skinny<E>(SK_RESID, reinterpret_cast<const E*>(h->dO), reinterpret_cast<const E*>(w.wo), d, h->nq, S, er, s));
-  HIPCHK(launch_dec_norm<E>(a, false, w.g_ffn, c.rms_eps, Xn, s));
+  SkinnyEpi ex{};
+  ex.out = h->dPx; ex.ldo = d;
+  HIPCHK(launch_skinny<E>(SK_PARTIAL, reinterpret_cast<const E*>(h->dO), reinterpret_cast<const E*>(w.wo), d, h->nq, S, kSplitO, ex, s));
+  HIPCHK(launch_dec_norm<E>(a, false, kSplitO, w.g_ffn, c.rms_eps, Xn, s));
   SkinnyEpi eg{};
   eg.h = h->dHf; eg.ldh = dff;
-  HIPCHK(launch_skinny<E>(SK_SWIGLU, Xn, reinterpret_cast<const E*>(w.wgu), 2 * dff, d, S, eg, s));
-  HIPCHK(launch_skinny<E>(SK_RESID, reinterpret_cast<const E*>(h->dHf), reinterpret_cast<const E*>(w.wd), d, dff, S, er, s));
+  HIPCHK(launch_skinny<E>(SK_SWIGLU, Xn, reinterpret_cast<const E*>(w.wgu), 2 * dff, d, S, 1, eg, s));
+  HIPCHK(launch_skinny<E>(SK_PARTIAL, reinterpret_cast<const E*>(h->dHf), reinterpret_cast<const E*>(w.wd), d, dff, S, kSplitDown, ex, s));
   return MOR_OK;
 }
 
@@ -471,17 +486,52 @@ template <typename E>
 mor_status dec_iteration(mor_handle_s* h, hipStream_t s) {
   const int n_s = h->n_s;
   HIPCHK(launch_dec_schedule(h->dec, s));
-  mor_status st = dec_layer<E>(h, h->blk[0], DL_FIRST, 0, s);
+  mor_status st = dec_layer<E>(h, h->blk[0], DL_FIRST, 0, 0, s);
   if (st != MOR_OK) return st;
-  HIPCHK(launch_dec_prep(h->dec, s));
+  HIPCHK(launch_dec_prep(h->dec, kSplitDown, s));      // X of new tokens += first layer's down
   for (int j = 1; j <= n_s; ++j) {
-    st = dec_layer<E>(h, h->blk[j], DL_SHARED, j, s);
+    st = dec_layer<E>(h, h->blk[j], DL_SHARED, j, j == 1 ? 0 : kSplitDown, s);
     if (st != MOR_OK) return st;
   }
-  HIPCHK(launch_dec_update(h->dec, s));
-  st = dec_layer<E>(h, h->blk[n_s + 1], DL_LAST, 0, s);
+  HIPCHK(launch_dec_update(h->dec, kSplitDown, s));    // F(H) = X + last shared layer's down
+  st = dec_layer<E>(h, h->blk[n_s + 1], DL_LAST, 0, 0, s);
   if (st != MOR_OK) return st;
-  HIPCHK(launch_dec_output(h->dec, s));
+  HIPCHK(launch_dec_output(h->dec, kSplitDown, s));    // output = X + last layer's down
+  return MOR_OK;
+}
+
+// Iterations per captured graph, and the switch that turns graphs off (MOR_DECODE_GRAPH=0).
+constexpr int kGraphIters = 8;
+bool use_graph() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("MOR_DECODE_GRAPH");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on == 1;
+}
+
+void drop_graph(mor_handle_s* h) {
+  if (h->dec_exec) (void)hipGraphExecDestroy(h->dec_exec);
+  if (h->dec_graph) (void)hipGraphDestroy(h->dec_graph);
+  h->dec_exec = nullptr;
+  h->dec_graph = nullptr;
+}
+
+// Records kGraphIters decode iterations (fixed grids, arguments fixed per submission) on a
+// private stream; the graph is then launched on the caller's stream.
+mor_status capture_graph(mor_handle_s* h) {
+  if (!h->cap_stream) HIPCHK(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
+  HIPCHK(hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeRelaxed));
+  mor_status st = MOR_OK;
+  for (int i = 0; i < kGraphIters && st == MOR_OK; ++i)
+    st = h->cfg.dtype == MOR_BF16 ? dec_iteration<bf16>(h, h->cap_stream) : dec_iteration<float>(h, h->cap_stream);
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(h->cap_stream, &g);
+  if (st != MOR_OK) { if (g) (void)hipGraphDestroy(g); return st; }
+  if (e != hipSuccess) return fail(MOR_E_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+  h->dec_graph = g;
+  HIPCHK(hipGraphInstantiate(&h->dec_exec, g, nullptr, nullptr, 0));
   return MOR_OK;
 }
 
@@ -567,7 +617,8 @@ mor_status mor_init(const mor_config* cfg, const mor_weights* w, void* workspace
   if (e == hipSuccess && h->decode) {
     const int d = cfg->d_model;
     e = hipMemsetAsync(h->dXn, 0, 64 * (size_t)d * h->es, s);
-    if (e == hipSuccess) e = hipMemsetAsync(h->dQkv, 0, 64 * (size_t)h->nqkv * 4, s);
+    if (e == hipSuccess) e = hipMemsetAsync(h->dQkv, 0, 4 * 64 * (size_t)h->nqkv * 4, s);
+    if (e == hipSuccess) e = hipMemsetAsync(h->dPx, 0, 8 * 64 * (size_t)d * 4, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->dO, 0, 64 * (size_t)h->nq * h->es, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->dHf, 0, 64 * (size_t)cfg->d_ff * h->es, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->dec.glob, 0, G_COUNT * 4, s);
@@ -666,6 +717,7 @@ mor_status mor_decode_submit(mor_handle* h, int32_t n_req, const int32_t* length
   if (z_dump) HIPCHK(launch_fill_f32(z_dump, (size_t)total * c.n_rec, NAN, s));
   HIPCHK(launch_dec_reset(a, n_req, s));
   HIPCHK(hipStreamSynchronize(s));   // the host copies above read pageable memory
+  drop_graph(h);                     // its kernel arguments name the previous submission's buffers
   h->submitted = true;
   return MOR_OK;
 }
@@ -675,7 +727,15 @@ mor_status mor_decode_step(mor_handle* h, int32_t n_iters, void* stream, int32_t
   if (!h->decode || !h->submitted) return fail(MOR_E_STATE, "no decode submission on this handle");
   if (n_iters < 0) return fail(MOR_E_INVALID, "n_iters < 0");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  for (int i = 0; i < n_iters; ++i) {
+  int done = 0;
+  if (n_iters >= kGraphIters && use_graph()) {
+    if (!h->dec_exec) {
+      mor_status st = capture_graph(h);
+      if (st != MOR_OK) return st;
+    }
+    for (; done + kGraphIters <= n_iters; done += kGraphIters) HIPCHK(hipGraphLaunch(h->dec_exec, s));
+  }
+  for (; done < n_iters; ++done) {
     const mor_status st = h->cfg.dtype == MOR_BF16 ? dec_iteration<bf16>(h, s) : dec_iteration<float>(h, s);
     if (st != MOR_OK) return st;
   }
@@ -737,6 +797,8 @@ mor_status mor_timing_read(mor_handle* h, double* total_ms, int32_t* launches) {
 
 void mor_destroy(mor_handle* h) {
   if (!h) return;
+  drop_graph(h);
+  if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
   for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
   delete h;
 }

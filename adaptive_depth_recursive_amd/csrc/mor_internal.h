@@ -121,7 +121,9 @@ struct DecArgs {
   const float* rope_cos;               // [max_seq][hd/2]
   const float* rope_sin;
   void* pool;                          // KV pages
-  const float* qkv;                    // [64][nqkv] fp32 projections (before RoPE)
+  const float* qkv;                    // [kqkv][64][nqkv] fp32 partial sums of the QKV projection
+  int kqkv;                            // K splits of the QKV projection
+  const float* px;                     // [<=8][64][d] fp32 partial sums of the O / down projections
   void* o;                             // [64][nq] attention output
   float scale_log2;
   // algorithmic bytes of the iterations (measurement): weights of every layer that runs, K/V
@@ -133,25 +135,28 @@ struct DecArgs {
 enum { ST_WEIGHT = 0, ST_KV_READ = 1, ST_KV_WRITE = 2, ST_ACT = 3, ST_COUNT = 4 };
 
 hipError_t launch_dec_schedule(const DecArgs& a, hipStream_t s);
+// `fold` = number of residual partial sums (DecArgs::px) to add into X before the kernel's work.
 template <typename T>
-hipError_t launch_dec_norm(const DecArgs& a, bool gather_inputs, const float* g, float eps, T* Xn,
-                           hipStream_t s);
-hipError_t launch_dec_prep(const DecArgs& a, hipStream_t s);
-hipError_t launch_dec_update(const DecArgs& a, hipStream_t s);
-hipError_t launch_dec_output(const DecArgs& a, hipStream_t s);
+hipError_t launch_dec_norm(const DecArgs& a, bool gather_inputs, int fold, const float* g,
+                           float eps, T* Xn, hipStream_t s);
+hipError_t launch_dec_prep(const DecArgs& a, int fold, hipStream_t s);
+hipError_t launch_dec_update(const DecArgs& a, int fold, hipStream_t s);
+hipError_t launch_dec_output(const DecArgs& a, int fold, hipStream_t s);
 template <typename T>
 hipError_t launch_dec_attn(const DecArgs& a, int kind, int j, hipStream_t s);
 hipError_t launch_dec_reset(const DecArgs& a, int n_req, hipStream_t s);
 
 // Skinny projections of the decode batch: out^T = W . A^T for the 64 slot rows of A.
-enum { SK_STORE = 0, SK_RESID = 1, SK_SWIGLU = 2 };
+//  SK_PARTIAL: K is split over `ksplit` workgroup rows; split k writes its fp32 partial sum to
+//              out + k * 64 * ldo ([64][ldo]); the consumer adds the splits in order.
+//  SK_SWIGLU:  one split; SiLU(gate) * up in the element type into h [64][ldh].
+enum { SK_PARTIAL = 0, SK_SWIGLU = 2 };
 struct SkinnyEpi {
-  float* out; int ldo;                 // SK_STORE: fp32 [64][ldo]
-  float* x; int ldx;                   // SK_RESID: fp32 residual rows
-  void* h; int ldh;                    // SK_SWIGLU: SiLU(gate) * up in the element type
+  float* out; int ldo;
+  void* h; int ldh;
 };
 template <typename T>
-hipError_t launch_skinny(int epi, const T* A, const T* W, int N, int K, int M, const SkinnyEpi& ep,
-                         hipStream_t s);
+hipError_t launch_skinny(int epi, const T* A, const T* W, int N, int K, int M, int ksplit,
+                         const SkinnyEpi& ep, hipStream_t s);
 
 }  // namespace mor

@@ -232,3 +232,24 @@ def test_decode_full_size_sampled():
     say(f"[gpu] full-size decode: {int(lens.sum())} tokens, {res['iters']} iterations, "
         f"depths {np.bincount(res['depth'], minlength=cfg.n_rec + 1)[1:]}, worst rel err {worst:.2e}")
     model.close()
+
+
+def test_decode_graph_replay_matches_eager():
+    """Iterations replayed from the captured graph (steps of 16) give the same bits as eager
+    launches (steps of 4, below the graph size), across many replays with host syncs between."""
+    import torch
+    cfg = workload.get_config("small_thr_bf16")
+    model, W, lens = _setup(cfg, slots=5)
+    inputs = workload.make_decode_inputs(cfg, lens)
+    x = torch.from_numpy(np.concatenate(inputs)).cuda()
+    res = []
+    for chunk in (4, 16):
+        out = torch.zeros_like(x)
+        dep = torch.zeros(x.shape[0], dtype=torch.int8, device="cuda")
+        model.decode_submit(lens, x, out, dep)
+        model.decode_run(x.shape[0], chunk=chunk, max_iters=x.shape[0] * cfg.n_rec + 1000)
+        torch.cuda.synchronize()
+        res.append((out.cpu().numpy(), dep.cpu().numpy()))
+    assert np.array_equal(res[0][1], res[1][1])
+    assert np.array_equal(res[0][0].view(np.uint32), res[1][0].view(np.uint32))
+    model.close()
