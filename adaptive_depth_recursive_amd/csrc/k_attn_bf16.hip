@@ -48,6 +48,19 @@ __device__ __forceinline__ void dma_rows(const bf16* src, size_t ld, char* dst, 
   }
 }
 
+// Maximum of finite-or-minus-infinity scores: v_max3 / v_max straight on the values (the
+// compiler's fmaxf first quiets possible NaNs, which these scores never are).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ bf16x8 rd(const char* base, int row, int chunk, int sw) {
   return *reinterpret_cast<const bf16x8*>(base + row * kRow + ((chunk ^ sw) << 4));
 }
@@ -154,14 +167,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
 
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
+      // the four key blocks are independent: issue their first K halves, then their second
       f32x4 s[4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 4; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][0], qf[hh][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][ks], qf[hh][ks], s[kb], 0, 0, 0);
-      }
+      for (int kb = 0; kb < 4; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][1], qf[hh][1], s[kb], 0, 0, 0);
       // s[kb][e] holds the raw score of key 32 (kb/2) + 8 g + 4 (kb & 1) + e of this tile
       if (need_mask) {
 #pragma unroll
@@ -169,12 +182,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[kb][e] = kpv[kb][e] > myqpos ? -INFINITY : s[kb][e];
       }
-      float mraw = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
-#pragma unroll
-      for (int kb = 1; kb < 4; ++kb)
-        mraw = fmaxf(mraw, fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3])));
-      mraw = fmaxf(mraw, __shfl_xor(mraw, 16));
-      mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+      float mraw = max3f(max3f(s[0][0], s[0][1], s[0][2]), max3f(s[0][3], s[1][0], s[1][1]),
+                         max3f(s[1][2], s[1][3], s[2][0]));
+      mraw = max3f(mraw, max3f(s[2][1], s[2][2], s[2][3]), max3f(s[3][0], s[3][1], s[3][2]));
+      mraw = max2f(mraw, s[3][3]);
+      mraw = max2f(mraw, __shfl_xor(mraw, 16));
+      mraw = max2f(mraw, __shfl_xor(mraw, 32));
       const float mloc = mraw * sl2;                   // scores enter the exponent scaled by sl2
       if (__any(mloc > mrun[hh] + 8.f)) {              // raise the reference maximum, rescale
         const float mnew = fmaxf(mrun[hh], mloc);
@@ -185,17 +198,20 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
         mrun[hh] = mnew;
       }
       const float nm = -mrun[hh];
-      float lsum = 0.f;
+      float pr[4][4];
       bf16x8 pf[2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][e], sl2, nm));
-          lsum += p;
-          pf[kb >> 1][4 * (kb & 1) + e] = (bf16)p;
+          pr[kb][e] = __builtin_amdgcn_exp2f(fmaf(s[kb][e], sl2, nm));
+          pf[kb >> 1][4 * (kb & 1) + e] = (bf16)pr[kb][e];
         }
-      lrun[hh] += lsum;
+      // row sum as a tree (short dependency chains)
+      float ls[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) ls[kb] = (pr[kb][0] + pr[kb][1]) + (pr[kb][2] + pr[kb][3]);
+      lrun[hh] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
