@@ -298,10 +298,10 @@ class Mor:
 
     def decode_stats(self, stream=None) -> Dict[str, int]:
         """mor_decode_stats as a dict (synchronises)."""
-        out = (ctypes.c_int64 * 8)()
+        out = (ctypes.c_int64 * 10)()
         _check(lib().mor_decode_stats(self.handle, _stream(stream), out))
         keys = ("tokens", "requests", "admitted", "iterations", "weight_bytes", "kv_read_bytes",
-                "kv_write_bytes", "act_bytes")
+                "kv_write_bytes", "act_bytes", "kv_pages_peak", "page_bytes")
         return dict(zip(keys, (int(v) for v in out)))
 
     def decode_run(self, total_tokens: int, chunk: int = 32, max_iters: int = 1 << 22, stream=None):

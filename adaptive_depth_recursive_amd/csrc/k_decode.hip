@@ -181,6 +181,7 @@ __global__ __launch_bounds__(64) void k_dec_schedule(DecArgs a) {
       atomicOr(a.err, (unsigned)ERR_KV_FULL);
     } else {
       g[G_TOP] = top - tot_need;
+      g[G_PEAK] = max(g[G_PEAK], a.kv_pages - (top - tot_need));
     }
   }
 }

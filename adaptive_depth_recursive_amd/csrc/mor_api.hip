@@ -764,6 +764,8 @@ mor_status mor_decode_stats(mor_handle* h, void* stream, int64_t* out) {
   HIPCHK(hipStreamSynchronize(s));
   out[0] = g[G_TOKENS]; out[1] = g[G_REQS]; out[2] = g[G_NEXT]; out[3] = g[G_ITER];
   for (int i = 0; i < ST_COUNT; ++i) out[4 + i] = (int64_t)st[i];
+  out[8] = g[G_PEAK];
+  out[9] = (int64_t)h->page_bytes;
   return MOR_OK;
 }
 

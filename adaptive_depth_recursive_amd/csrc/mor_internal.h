@@ -80,7 +80,8 @@ hipError_t launch_pack_gate_up(const T* wg, const T* wu, T* out, int dff, int d,
 namespace mor {
 
 // Indices of the engine's global counters (DecArgs::glob).
-enum { G_NEXT = 0, G_TOP = 1, G_TOKENS = 2, G_REQS = 3, G_HALT = 4, G_NREQ = 5, G_ITER = 6, G_COUNT = 16 };
+enum { G_NEXT = 0, G_TOP = 1, G_TOKENS = 2, G_REQS = 3, G_HALT = 4, G_NREQ = 5, G_ITER = 6,
+       G_PEAK = 7, G_COUNT = 16 };  // G_PEAK: most pages in use at once
 // Error flag bits (shared with prefill's bit 0 = NaN router logit).
 enum { ERR_NAN_LOGIT = 1u, ERR_KV_FULL = 2u };
 // Layer kinds of one decode iteration: which slots take part and which cache stream they use.

@@ -110,16 +110,17 @@ def cpu_baseline(cfg, weights, H0_np, seq_len: int):
                       f"oracle in float64 with bf16 storage points; {dt:.1f} s"}
 
 
-def decode_bench(args):
+def decode_bench(args, kv_mode="recursion"):
     """Depth-wise batched MoR-4 decode of the 360M-shape model (51 slots, 1024 requests with
     Geometric(mean 256) lengths, threshold exit with the calibrated router biases). Timed over
-    the steady-state window: iterations while the request queue is not empty (every slot busy)."""
+    the steady-state window: iterations while the request queue is not empty (every slot busy).
+    kv_mode "share" runs recursive KV sharing (recursions >= 2 read the recursion-1 cache)."""
     import numpy as np
     import torch
     import adaptive_depth_recursive_amd as mor
     import workload
 
-    cfg = workload.get_config("smol360m_mor4_decode")
+    cfg = workload.get_config("smol360m_mor4_decode", kv_mode=kv_mode)
     W = workload.make_weights(cfg)
     with open(os.path.join(ROOT, "tests", "golden", "decode_router_bias.json")) as f:
         W["router_b"] = np.array(json.load(f)["router_b"], np.float32)
@@ -149,6 +150,7 @@ def decode_bench(args):
     kvr = last["kv_read_bytes"] - st0["kv_read_bytes"]
     s_ = ms / 1e3
     done = dep[dep > 0].cpu().numpy()
+    peak_pages = last["kv_pages_peak"]
     model.close()
     return {
         "metric": "MoR-4 decode tokens/sec (360M-shape, 51 slots, depth-wise batching, bf16)",
@@ -161,9 +163,10 @@ def decode_bench(args):
                      "algorithmic_bytes_per_iteration": byt / max(it, 1),
                      "kv_read_bytes_per_iteration": kvr / max(it, 1)},
         "exit_depth_histogram": np.bincount(done, minlength=cfg.n_rec + 1)[1:].tolist(),
+        "kv_cache_peak_bytes": peak_pages * last["page_bytes"],
         "config": {"workload": f"{cfg.name}: d {cfg.d_model}, {cfg.n_q_heads}/{cfg.n_kv_heads} heads x "
                                f"{cfg.head_dim}, FFN {cfg.d_ff}, L {cfg.n_layers} (N_r {cfg.n_rec} x "
-                               f"{cfg.n_shared} shared), threshold exit, {cfg.slots} slots, "
+                               f"{cfg.n_shared} shared), threshold exit, {cfg.kv_mode}-wise KV, {cfg.slots} slots, "
                                f"{len(lens)} requests, {int(lens.sum())} tokens, "
                                f"{args.kv_page_tokens}-token KV pages"},
     }
@@ -184,6 +187,8 @@ def main():
     ap.add_argument("--decode-chunk", type=int, default=64)
     ap.add_argument("--decode-warmup", type=int, default=64)
     ap.add_argument("--kv-page-tokens", type=int, default=64)
+    ap.add_argument("--decode-kv", default="recursion", choices=["recursion", "share"],
+                    help="KV mode of --decode-only")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -210,7 +215,7 @@ def main():
         return
 
     if args.decode_only:
-        print(json.dumps(decode_bench(args)), flush=True)
+        print(json.dumps(decode_bench(args, args.decode_kv)), flush=True)
         return
 
     cfg = workload.get_config(args.config)
@@ -285,7 +290,9 @@ def main():
     del h, h_out
     torch.cuda.empty_cache()
     if not args.no_decode:
-        result["decode"] = decode_bench(args)
+        result["decode"] = decode_bench(args, "recursion")
+        torch.cuda.empty_cache()
+        result["decode_kv_share"] = decode_bench(args, "share")
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, W, H0, args.cpu_seq)

@@ -218,7 +218,8 @@ mor_status mor_decode_step(mor_handle* h, int32_t n_iters, void* stream, int32_t
  *   out[0] tokens finished, out[1] requests finished, out[2] requests admitted from the queue,
  *   out[3] iterations run, then the algorithmic bytes of those iterations: out[4] weights (every
  *   layer that ran for at least one token, once per iteration), out[5] K/V read from the cache,
- *   out[6] K/V appended, out[7] input and output rows. */
+ *   out[6] K/V appended, out[7] input and output rows; out[8] the most KV pages in use at once,
+ *   out[9] bytes per page. out has room for 10 values. */
 mor_status mor_decode_stats(mor_handle* h, void* stream, int64_t* out);
 
 /* Frees the host-side handle. The workspace stays the caller's. NULL is ignored. */
