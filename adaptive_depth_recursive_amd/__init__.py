@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.mor_timing_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
         L.mor_decode_submit.restype = i32
         L.mor_decode_submit.argtypes = [vp, i32, ctypes.POINTER(i32), vp, vp, vp, vp, vp, vp]
+        L.mor_decode_continue.restype = i32
+        L.mor_decode_continue.argtypes = [vp, i32, ctypes.POINTER(i32), vp, vp, vp, vp, vp, vp]
         L.mor_decode_step.restype = i32
         L.mor_decode_step.argtypes = [vp, i32, vp, ctypes.POINTER(i32)]
         L.mor_decode_stats.restype = i32
@@ -101,7 +103,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("mor_abi_version", "mor_last_error", "mor_workspace_bytes", "mor_init",
             "mor_prefill", "mor_route", "mor_kv_view", "mor_get_error_flags", "mor_timing_enable",
-            "mor_timing_read", "mor_decode_submit", "mor_decode_step", "mor_decode_stats", "mor_destroy")
+            "mor_timing_read", "mor_decode_submit", "mor_decode_continue", "mor_decode_step", "mor_decode_stats",
+            "mor_destroy")
 KERNEL_KINDS = {"qkv": 1, "attention": 2, "o_proj": 3, "gate_up": 4, "down": 5}
 
 
@@ -282,6 +285,17 @@ class Mor:
         lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
         self._dec_keep = (inputs, outputs, exit_depth, h_dump, z_dump)
         _check(lib().mor_decode_submit(
+            self.handle, int(lens.size), lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            inputs.data_ptr(), outputs.data_ptr(), exit_depth.data_ptr(), _ptr(h_dump),
+            _ptr(z_dump), _stream(stream)))
+
+    def decode_continue(self, lengths, inputs, outputs, exit_depth, h_dump=None, z_dump=None,
+                        stream=None):
+        """mor_decode_continue: request b continues sequence b of the last prefill."""
+        import numpy as np
+        lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+        self._dec_keep = (inputs, outputs, exit_depth, h_dump, z_dump)
+        _check(lib().mor_decode_continue(
             self.handle, int(lens.size), lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
             inputs.data_ptr(), outputs.data_ptr(), exit_depth.data_ptr(), _ptr(h_dump),
             _ptr(z_dump), _stream(stream)))

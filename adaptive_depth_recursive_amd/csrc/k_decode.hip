@@ -69,7 +69,7 @@ __global__ __launch_bounds__(64) void k_dec_schedule(DecArgs a) {
       admit = true;
     } else {
       finished = true;
-      const int len = a.req_len[req];
+      const int len = a.sl_base[s] + a.req_len[req];
       nfree = 2 * ((len + a.P - 1) / a.P);
       for (int r = 1; r <= a.R; ++r)
         if (!a.kv_share || r == 1) nfree += a.n_s * ((a.sl_cnt[s * a.R + r - 1] + a.P - 1) / a.P);
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(64) void k_dec_schedule(DecArgs a) {
     for (int ls = 0; ls < a.LS; ++ls) {
       int n;
       if (ls < 2) {
-        n = (a.req_len[req] + a.P - 1) / a.P;
+        n = (a.sl_base[s] + a.req_len[req] + a.P - 1) / a.P;
       } else {
         const int r = (ls - 2) / a.n_s + 1;
         n = (a.kv_share && r > 1) ? 0 : (a.sl_cnt[s * a.R + r - 1] + a.P - 1) / a.P;
@@ -104,16 +104,18 @@ __global__ __launch_bounds__(64) void k_dec_schedule(DecArgs a) {
     req = next + rank;
     pos = 0;
     admit = true;
+    a.sl_base[s] = 0;
     for (int r = 0; r < a.R; ++r) a.sl_cnt[s * a.R + r] = 0;
   }
   const int taken = min(nfreeslots, max(0, nreq - next));
 
   const bool part = valid && req >= 0;
   const int r = admit ? 1 : depth;
+  const int kpos = (part ? a.sl_base[s] : 0) + pos;   // cache index of the token in the unique layers
   int need = 0;
   bool need_u = false, need_s = false;
   if (part) {
-    need_u = admit && (pos % a.P == 0);
+    need_u = admit && (kpos % a.P == 0);
     need_s = (!a.kv_share || r == 1) && (a.sl_cnt[s * a.R + r - 1] % a.P == 0);
     need = (need_u ? 2 : 0) + (need_s ? a.n_s : 0);
   }
@@ -123,8 +125,8 @@ __global__ __launch_bounds__(64) void k_dec_schedule(DecArgs a) {
   if (!full && part) {
     int p = top - tot_need + off;
     if (need_u) {
-      a.ptab[((size_t)s * a.LS + 0) * a.pps + pos / a.P] = a.free_pages[p++];
-      a.ptab[((size_t)s * a.LS + 1) * a.pps + pos / a.P] = a.free_pages[p++];
+      a.ptab[((size_t)s * a.LS + 0) * a.pps + kpos / a.P] = a.free_pages[p++];
+      a.ptab[((size_t)s * a.LS + 1) * a.pps + kpos / a.P] = a.free_pages[p++];
     }
     if (need_s) {
       const int idx = a.sl_cnt[s * a.R + r - 1] / a.P;
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(64) void k_dec_schedule(DecArgs a) {
   int n_first = 0, n_part = 0;
   if (!full && part) {
     const int idx = a.sl_cnt[s * a.R + r - 1];
-    if (admit) { kv_rd += (long long)pos * kvtok; kv_wr += kvtok; act += 4LL * a.d; n_first = 1; }
+    if (admit) { kv_rd += (long long)kpos * kvtok; kv_wr += kvtok; act += 4LL * a.d; n_first = 1; }
     if (a.kv_share && r >= 2) {
       kv_rd += (long long)a.n_s * (a.sl_cnt[s * a.R] ) * kvtok;
     } else {
@@ -196,7 +198,7 @@ __global__ void k_dec_reset(DecArgs a, int n_req) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < a.kv_pages) a.free_pages[i] = a.kv_pages - 1 - i;
   if (i < a.S) {
-    a.sl_req[i] = -1; a.sl_pos[i] = 0; a.sl_depth[i] = 0;
+    a.sl_req[i] = -1; a.sl_pos[i] = 0; a.sl_base[i] = 0; a.sl_depth[i] = 0;
     a.sl_first[i] = 0; a.sl_part[i] = 0; a.sl_exit[i] = 0;
     for (int r = 0; r < a.R; ++r) a.sl_cnt[i * a.R + r] = 0;
   }
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_output(DecArgs a, int fold)
     // last-layer bytes of this iteration (every slot's exit flag is still set here)
     const long long kvtok = 2LL * a.hkv * a.hd * a.es;
     const bool ex = t < a.S && a.sl_exit[t];
-    long long rd = ex ? (long long)a.sl_pos[t] * kvtok : 0;
+    long long rd = ex ? (long long)(a.sl_base[t] + a.sl_pos[t]) * kvtok : 0;
     int n = ex ? 1 : 0;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -474,7 +476,7 @@ __global__ __launch_bounds__(DA_WAVES * 64) void k_dec_attn(DecArgs a, int kind,
   const int part = kind == DL_FIRST ? a.sl_first[s] : kind == DL_LAST ? a.sl_exit[s] : a.sl_part[s];
   if (!part) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int pos = a.sl_pos[s], r = a.sl_depth[s];
+  const int pos = a.sl_base[s] + a.sl_pos[s], r = a.sl_depth[s];   // position in the sequence
   int ls_w, ls_r, idx_w, nkeys;
   if (kind == DL_FIRST || kind == DL_LAST) {
     ls_w = ls_r = (kind == DL_FIRST) ? 0 : 1;
@@ -644,6 +646,83 @@ hipError_t launch_dec_attn(const DecArgs& a, int kind, int j, hipStream_t s) {
 }
 template hipError_t launch_dec_attn<float>(const DecArgs&, int, int, hipStream_t);
 template hipError_t launch_dec_attn<bf16>(const DecArgs&, int, int, hipStream_t);
+
+// ------------------------------------------------------------------ hand-over from a prefill
+// Slot b takes request b, whose first T positions were computed by the prefill: its per-stream
+// page lists are allocated in slot order from the free stack (one thread, in order), its
+// recursion counts are the prefill's, and the next schedule admits its first decoded token at
+// position T. Then every cached K/V row of the prefill is copied to its page (V transposed back).
+__global__ void k_dec_prefix_alloc(DecArgs a, PrefixSrc p) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int top = a.glob[G_TOP];
+  for (int b = 0; b < p.B; ++b) {
+    a.sl_req[b] = b; a.sl_pos[b] = -1; a.sl_base[b] = p.T; a.sl_depth[b] = 0;
+    for (int r = 0; r < a.R; ++r) a.sl_cnt[b * a.R + r] = p.cnt[r * p.cnt_ld + b];
+    for (int ls = 0; ls < a.LS; ++ls) {
+      int n;
+      if (ls < 2) {
+        n = p.T;
+      } else {
+        const int r = (ls - 2) / a.n_s + 1;
+        n = (a.kv_share && r > 1) ? 0 : a.sl_cnt[b * a.R + r - 1];
+      }
+      const int np = (n + a.P - 1) / a.P;
+      for (int i = 0; i < np; ++i) {
+        if (top == 0) { a.glob[G_HALT] = 1; atomicOr(a.err, (unsigned)ERR_KV_FULL); a.glob[G_TOP] = 0; return; }
+        a.ptab[((size_t)b * a.LS + ls) * a.pps + i] = a.free_pages[--top];
+      }
+    }
+  }
+  a.glob[G_TOP] = top;
+  a.glob[G_NEXT] = p.B;
+  a.glob[G_PEAK] = a.kv_pages - top;
+}
+
+// One thread per (sequence, prefill stream, cached row, element of K or V).
+template <typename T>
+__global__ void k_dec_prefix_copy(DecArgs a, PrefixSrc p, int nstreams) {
+  const int HDk = a.hd, row = a.hkv * HDk;
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long per_seq = (long long)nstreams * p.T * 2 * row;
+  if (i >= per_seq * p.B || a.glob[G_HALT]) return;
+  const int b = (int)(i / per_seq);
+  long long rem = i - b * per_seq;
+  const int ps = (int)(rem / ((long long)p.T * 2 * row));
+  rem -= (long long)ps * p.T * 2 * row;
+  const int idx = (int)(rem / (2 * row));
+  const int e = (int)(rem - (long long)idx * 2 * row);
+  const bool isv = e >= row;
+  const int h = (e % row) / HDk, c = e % HDk;
+  // prefill stream -> layer stream and number of cached rows
+  const int last = nstreams - 1;
+  int ls, n;
+  if (ps == 0) { ls = 0; n = p.T; }
+  else if (ps == last) { ls = 1; n = p.T; }
+  else {
+    const int r = (ps - 1) / a.n_s + 1;
+    ls = ps + 1;
+    n = (a.kv_share && r > 1) ? 0 : p.cnt[(r - 1) * p.cnt_ld + b];
+  }
+  if (idx >= n) return;
+  const T* k = reinterpret_cast<const T*>(reinterpret_cast<const char*>(p.kv) + (size_t)ps * 2 * p.half_bytes);
+  const T* vt = reinterpret_cast<const T*>(reinterpret_cast<const char*>(p.kv) + ((size_t)ps * 2 + 1) * p.half_bytes);
+  const T v = isv ? vt[(((size_t)b * a.hkv + h) * HDk + c) * p.kpad + idx]
+                  : k[((size_t)b * p.kpad + idx) * row + h * HDk + c];
+  const int page = a.ptab[((size_t)b * a.LS + ls) * a.pps + idx / a.P];
+  T* dst = reinterpret_cast<T*>(a.pool) + (size_t)page * a.page_elems + (isv ? (size_t)a.hkv * a.P * HDk : 0) +
+           ((size_t)h * a.P + idx % a.P) * HDk + c;
+  *dst = v;
+}
+
+hipError_t launch_dec_prefix(const DecArgs& a, const PrefixSrc& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_dec_prefix_alloc, dim3(1), dim3(64), 0, s, a, p);
+  const int nstreams = 2 + a.R * a.n_s;
+  const long long total = (long long)p.B * nstreams * p.T * 2 * a.hkv * a.hd;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (a.es == 2) hipLaunchKernelGGL((k_dec_prefix_copy<bf16>), dim3(blocks), dim3(256), 0, s, a, p, nstreams);
+  else hipLaunchKernelGGL((k_dec_prefix_copy<float>), dim3(blocks), dim3(256), 0, s, a, p, nstreams);
+  return hipGetLastError();
+}
 
 // ------------------------------------------------------------------ skinny projections
 // out^T = W . A^T for the 64 rows of A (the slots), weights on the MFMA A side. A workgroup owns

@@ -103,6 +103,7 @@ struct mor_handle_s {
   void* dO = nullptr;            // [64][nq]
   void* dHf = nullptr;           // [64][d_ff]
   bool submitted = false;
+  int last_B = 0, last_T = 0;    // shape of the last mor_prefill (the prefix a decode can continue)
   // decode iterations replayed as a captured HIP graph (kernel arguments fixed per submission)
   hipStream_t cap_stream = nullptr;
   hipGraph_t dec_graph = nullptr;
@@ -214,6 +215,7 @@ size_t plan(const mor_config& c, mor_handle_s* h, char* base) {
   float* dPx = nullptr;
   if (S) {
     da.sl_req = cur.take<int>(S * 4); da.sl_pos = cur.take<int>(S * 4);
+    da.sl_base = cur.take<int>(S * 4);
     da.sl_depth = cur.take<int>(S * 4); da.sl_first = cur.take<int>(S * 4);
     da.sl_part = cur.take<int>(S * 4); da.sl_exit = cur.take<int>(S * 4);
     da.sl_cnt = cur.take<int>((size_t)S * R * 4);
@@ -640,9 +642,12 @@ mor_status mor_prefill(mor_handle* h, const float* h_in, int32_t B, int32_t T, f
   if (B < 1 || B > h->cfg.max_batch || T < 1 || T > h->cfg.max_seq)
     return fail(MOR_E_SHAPE, "B or T outside 1..max_batch / 1..max_seq");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (h->cfg.dtype == MOR_BF16)
-    return prefill_impl<bf16>(h, h_in, B, T, h_out, sel_pos, counts, logits, h_per_rec, s);
-  return prefill_impl<float>(h, h_in, B, T, h_out, sel_pos, counts, logits, h_per_rec, s);
+  h->last_B = 0;
+  const mor_status st = h->cfg.dtype == MOR_BF16
+                            ? prefill_impl<bf16>(h, h_in, B, T, h_out, sel_pos, counts, logits, h_per_rec, s)
+                            : prefill_impl<float>(h, h_in, B, T, h_out, sel_pos, counts, logits, h_per_rec, s);
+  if (st == MOR_OK) { h->last_B = B; h->last_T = T; }
+  return st;
 }
 
 mor_status mor_route(mor_handle* h, const float* H, const int32_t* active_in,
@@ -690,9 +695,15 @@ mor_status mor_get_error_flags(mor_handle* h, void* stream, uint32_t* flags) {
   return MOR_OK;
 }
 
-mor_status mor_decode_submit(mor_handle* h, int32_t n_req, const int32_t* lengths,
-                             const float* inputs, float* outputs, int8_t* exit_depth,
-                             float* h_dump, float* z_dump, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared part of mor_decode_submit / mor_decode_continue: validates, uploads the request
+// table, resets the engine; with prefix_T > 0 the requests continue the last prefill's sequences.
+mor_status decode_begin(mor_handle* h, int32_t n_req, const int32_t* lengths, const float* inputs,
+                        float* outputs, int8_t* exit_depth, float* h_dump, float* z_dump,
+                        int prefix_T, void* stream) {
   if (!h) return fail(MOR_E_INVALID, "null handle");
   if (!h->decode) return fail(MOR_E_STATE, "handle was planned without decode state (max_slots = 0)");
   if (n_req < 1 || !lengths || !inputs || !outputs || !exit_depth)
@@ -702,7 +713,8 @@ mor_status mor_decode_submit(mor_handle* h, int32_t n_req, const int32_t* length
   std::vector<int32_t> off(n_req);
   long long total = 0;
   for (int i = 0; i < n_req; ++i) {
-    if (lengths[i] < 1 || lengths[i] > c.max_seq) return fail(MOR_E_SHAPE, "request length outside 1..max_seq");
+    if (lengths[i] < 1 || prefix_T + lengths[i] > c.max_seq)
+      return fail(MOR_E_SHAPE, "request length outside 1..max_seq (prefix included)");
     off[i] = (int32_t)total;
     total += lengths[i];
   }
@@ -716,10 +728,36 @@ mor_status mor_decode_submit(mor_handle* h, int32_t n_req, const int32_t* length
   HIPCHK(hipMemcpyAsync(h->dreq_off, off.data(), (size_t)n_req * 4, hipMemcpyHostToDevice, s));
   if (z_dump) HIPCHK(launch_fill_f32(z_dump, (size_t)total * c.n_rec, NAN, s));
   HIPCHK(launch_dec_reset(a, n_req, s));
+  if (prefix_T > 0) {
+    PrefixSrc p{h->kv, h->kv_half_bytes, h->kpad, h->cnt + c.max_batch, c.max_batch, n_req, prefix_T};
+    HIPCHK(launch_dec_prefix(a, p, s));
+  }
   HIPCHK(hipStreamSynchronize(s));   // the host copies above read pageable memory
   drop_graph(h);                     // its kernel arguments name the previous submission's buffers
   h->submitted = true;
   return MOR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mor_status mor_decode_submit(mor_handle* h, int32_t n_req, const int32_t* lengths,
+                             const float* inputs, float* outputs, int8_t* exit_depth,
+                             float* h_dump, float* z_dump, void* stream) {
+  return decode_begin(h, n_req, lengths, inputs, outputs, exit_depth, h_dump, z_dump, 0, stream);
+}
+
+mor_status mor_decode_continue(mor_handle* h, int32_t n_req, const int32_t* lengths,
+                               const float* inputs, float* outputs, int8_t* exit_depth,
+                               float* h_dump, float* z_dump, void* stream) {
+  if (!h) return fail(MOR_E_INVALID, "null handle");
+  if (h->cfg.routing != MOR_ROUTE_THRESHOLD || !h->decode)
+    return fail(MOR_E_STATE, "decode continuation needs a threshold-routed handle with decode state");
+  if (h->last_B == 0) return fail(MOR_E_STATE, "no prefill to continue on this handle");
+  if (n_req != h->last_B) return fail(MOR_E_SHAPE, "n_req must equal the batch of the last prefill");
+  if (n_req > h->cfg.max_slots) return fail(MOR_E_SHAPE, "n_req > max_slots");
+  return decode_begin(h, n_req, lengths, inputs, outputs, exit_depth, h_dump, z_dump, h->last_T, stream);
 }
 
 mor_status mor_decode_step(mor_handle* h, int32_t n_iters, void* stream, int32_t* progress) {

@@ -97,7 +97,8 @@ struct DecArgs {
   int kv_pages;
   // slot table
   int* sl_req;                         // request in the slot, -1 = free
-  int* sl_pos;                         // position of the token in flight
+  int* sl_pos;                         // index of the token in flight within the request
+  int* sl_base;                        // cached prefix of the request (its tokens sit at base + pos)
   int* sl_depth;                       // recursion the token runs this iteration (0 = token finished)
   int* sl_first;                       // token admitted this iteration (runs the first layer)
   int* sl_part;                        // slot runs the shared block this iteration
@@ -146,6 +147,13 @@ hipError_t launch_dec_output(const DecArgs& a, int fold, hipStream_t s);
 template <typename T>
 hipError_t launch_dec_attn(const DecArgs& a, int kind, int j, hipStream_t s);
 hipError_t launch_dec_reset(const DecArgs& a, int n_req, hipStream_t s);
+// Hand-over from a prefill: slot b takes request b with the T-token prefix of prefill sequence b.
+// `streams` points at the prefill cache streams (K [B][kpad][hkv][hd], V^T [B][hkv][hd][kpad]),
+// `cnt` at the prefill's per-recursion counts [N_r][max_batch].
+struct PrefixSrc {
+  const void* kv; size_t half_bytes; int kpad; const int* cnt; int cnt_ld; int B; int T;
+};
+hipError_t launch_dec_prefix(const DecArgs& a, const PrefixSrc& p, hipStream_t s);
 
 // Skinny projections of the decode batch: out^T = W . A^T for the 64 slot rows of A.
 //  SK_PARTIAL: K is split over `ksplit` workgroup rows; split k writes its fp32 partial sum to

@@ -207,6 +207,19 @@ mor_status mor_decode_submit(mor_handle* h, int32_t n_req, const int32_t* length
                              const float* inputs, float* outputs, int8_t* exit_depth,
                              float* h_dump, float* z_dump, void* stream);
 
+/* Prefill -> decode hand-over: the n_req requests continue the n_req sequences of the last
+ * mor_prefill on this handle (same batch B = n_req <= max_slots, threshold routing). Request b's
+ * tokens take positions T .. T + lengths[b] - 1 (T = the prefill's sequence length), and its
+ * attention at every layer and recursion also reads the K/V the prefill cached for sequence b at
+ * that layer and recursion (the prefill's caches are copied into the request's pages; slot b
+ * holds request b). With threshold routing the result equals the prefill of the whole sequence.
+ * Arguments and token-array layout as mor_decode_submit (rows are the continuation tokens only).
+ * Errors: MOR_E_STATE (no prefill, no decode state, or not threshold routing), MOR_E_SHAPE
+ * (n_req != prefill batch, n_req > max_slots, T + length > max_seq), MOR_E_INVALID, MOR_E_HIP. */
+mor_status mor_decode_continue(mor_handle* h, int32_t n_req, const int32_t* lengths,
+                               const float* inputs, float* outputs, int8_t* exit_depth,
+                               float* h_dump, float* z_dump, void* stream);
+
 /* Enqueues n_iters decode iterations on `stream` (no host synchronisation). If progress is not
  * NULL it then synchronises and writes {tokens finished, requests finished, iterations run} of
  * the current submission into progress[0..2].

@@ -253,3 +253,63 @@ def test_decode_graph_replay_matches_eager():
     assert np.array_equal(res[0][1], res[1][1])
     assert np.array_equal(res[0][0].view(np.uint32), res[1][0].view(np.uint32))
     model.close()
+
+
+@pytest.mark.parametrize("dtype,kv_mode", [("f32", "recursion"), ("bf16", "recursion"), ("f32", "share")])
+def test_decode_continues_prefill(dtype, kv_mode):
+    """Prefill -> decode hand-over: three prompts of 40 tokens are prefilled with threshold
+    routing, then decoded further (5, 17 and 9 tokens) from the prefill's per-recursion caches.
+    With threshold routing (causal) the result must equal the oracle's forward of each whole
+    sequence: fp32 free-running (exact depths), bf16 teacher-forced."""
+    import torch
+    import adaptive_depth_recursive_amd as mor
+    cfg = workload.get_config("small_thr_bf16", dtype=dtype, kv_mode=kv_mode)
+    W = workload.make_weights(cfg)
+    W["router_b"] = BIAS_SMALL
+    B, T = 3, 40
+    lens = np.array([5, 17, 9], np.int32)
+    say(f"[gpu] decode hand-over {dtype} {kv_mode}: prefill {B} x {T}, continue {lens.tolist()}")
+    model = mor.Mor(cfg, W, max_batch=B, max_seq=64, max_slots=B, kv_page_tokens=16, max_requests=B)
+    prompt = workload.make_inputs(cfg, batch=B, seq=T)
+    pre = model.prefill_outputs(torch.from_numpy(prompt).cuda(), debug=False)
+    torch.cuda.synchronize()
+    sel = pre["sel_pos"].cpu().numpy()
+    cnt = pre["counts"].cpu().numpy()
+    cont = workload.make_decode_inputs(cfg, lens)
+    x = torch.from_numpy(np.concatenate(cont)).cuda()
+    out = torch.zeros_like(x)
+    dep = torch.zeros(x.shape[0], dtype=torch.int8, device="cuda")
+    hd = torch.full((x.shape[0], cfg.n_rec + 1, cfg.d_model), np.nan, device="cuda")
+    zd = torch.empty((x.shape[0], cfg.n_rec), device="cuda")
+    model.decode_continue(lens, x, out, dep, hd, zd)
+    model.decode_run(x.shape[0], chunk=16, max_iters=4000)
+    done = model.decode_step(0, sync=True)
+    torch.cuda.synchronize()
+    assert done[0] == x.shape[0] and done[1] == B
+    res = {"out": out.cpu().numpy(), "depth": dep.cpu().numpy().astype(np.int32),
+           "h": hd.cpu().numpy(), "z": zd.cpu().numpy()}
+    _check_routing(cfg, W, res, lens)
+    offs = _offsets(lens)
+    for b in range(B):
+        n = int(lens[b])
+        full = np.concatenate([prompt[b], cont[b]])[None]
+        depth_c = res["depth"][offs[b]:offs[b] + n]
+        forced = None
+        if dtype == "bf16":
+            forced = []
+            for r in range(cfg.n_rec):
+                ps = sel[r, b, :cnt[r, b]]
+                forced.append([np.concatenate([ps, T + np.nonzero(depth_c >= r + 1)[0]])])
+        ref = oracle.prefill(cfg.replace(seq=T + n), W, full, forced_sel=forced)
+        p = ref["per_seq"][0]
+        if dtype == "f32":
+            own = np.zeros(T + n, np.int32)
+            for r, s_ in enumerate(p["own_sel"], start=1):
+                own[s_] = r
+            assert np.array_equal(own[T:], depth_c), f"seq {b}: continuation depths differ"
+            for r in range(cfg.n_rec):
+                assert np.array_equal(p["own_sel"][r][p["own_sel"][r] < T], sel[r, b, :cnt[r, b]])
+        e = rel_err(res["out"][offs[b]:offs[b] + n], ref["out"][0][T:])
+        say(f"[gpu] hand-over seq {b}: rel err {e:.2e}")
+        assert e <= tolerance(cfg), f"seq {b}: continuation output rel err {e}"
+    model.close()
