@@ -172,6 +172,62 @@ def decode_bench(args, kv_mode="recursion"):
     }
 
 
+def handoff_bench(args):
+    """Prefill -> decode hand-over on the 360M MoR-4 model: 51 prompts of 256 tokens prefilled with
+    the threshold router, their per-recursion caches handed to the decode engine
+    (mor_decode_continue), then the first 51 seeded continuations decoded to the end."""
+    import numpy as np
+    import torch
+    import adaptive_depth_recursive_amd as mor
+    import workload
+
+    cfg = workload.get_config("smol360m_mor4_decode")
+    W = workload.make_weights(cfg)
+    with open(os.path.join(ROOT, "tests", "golden", "decode_router_bias.json")) as f:
+        W["router_b"] = np.array(json.load(f)["router_b"], np.float32)
+    B, T = cfg.slots, 256
+    model = mor.Mor(cfg, W, max_batch=B, max_seq=cfg.max_len, max_slots=B,
+                    kv_page_tokens=args.kv_page_tokens, max_requests=B)
+    prompts = torch.from_numpy(workload.make_inputs(cfg, batch=B, seq=T)).cuda()
+    pout = torch.empty_like(prompts)
+    for _ in range(2):
+        model.prefill(prompts, pout)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    reps = 5
+    for _ in range(reps):
+        model.prefill(prompts, pout)
+    ev[1].record()
+    torch.cuda.synchronize()
+    pre_ms = ev[0].elapsed_time(ev[1]) / reps
+    counts = torch.empty((cfg.n_rec, B), dtype=torch.int32, device="cuda")
+    model.prefill(prompts, pout, counts=counts)
+    torch.cuda.synchronize()
+    cnt = counts.cpu().numpy()
+    lens = np.minimum(workload.make_decode_lengths(cfg)[:B], cfg.max_len - T)
+    x = torch.from_numpy(np.concatenate(workload.make_decode_inputs(cfg, lens))).cuda()
+    out = torch.empty_like(x)
+    dep = torch.zeros(x.shape[0], dtype=torch.int8, device="cuda")
+    t0 = time.perf_counter()
+    model.decode_continue(lens, x, out, dep)            # synchronises
+    hand_s = time.perf_counter() - t0
+    kvtok = 2 * cfg.n_kv_heads * cfg.head_dim * 2
+    kv_rows = B * T * 2 + cfg.n_shared * int(cnt.sum())  # first, last and every (r, j) stream
+    ev[0].record()
+    it = model.decode_run(int(lens.sum()), chunk=64)
+    ev[1].record()
+    torch.cuda.synchronize()
+    dec_ms = ev[0].elapsed_time(ev[1])
+    model.close()
+    return {"prompt": f"{B} x {T} tokens, threshold routing",
+            "prefill_ms": pre_ms, "prefill_tokens_per_s": B * T / pre_ms * 1e3,
+            "prompt_depth_counts": cnt.sum(axis=1).tolist(),
+            "handoff_ms_incl_host": hand_s * 1e3, "handoff_kv_bytes": kv_rows * kvtok,
+            "continuation_tokens": int(lens.sum()), "decode_iterations": it,
+            "decode_tokens_per_s_all": float(lens.sum()) / dec_ms * 1e3,
+            "note": "decode rate over all iterations, including the drain of the longest requests"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +243,7 @@ def main():
     ap.add_argument("--decode-chunk", type=int, default=64)
     ap.add_argument("--decode-warmup", type=int, default=64)
     ap.add_argument("--kv-page-tokens", type=int, default=64)
+    ap.add_argument("--handoff-only", action="store_true", help="only the prefill -> decode hand-over leg")
     ap.add_argument("--decode-kv", default="recursion", choices=["recursion", "share"],
                     help="KV mode of --decode-only")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -214,6 +271,9 @@ def main():
         print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4}))
         return
 
+    if args.handoff_only:
+        print(json.dumps(handoff_bench(args)), flush=True)
+        return
     if args.decode_only:
         print(json.dumps(decode_bench(args, args.decode_kv)), flush=True)
         return
@@ -293,6 +353,8 @@ def main():
         result["decode"] = decode_bench(args, "recursion")
         torch.cuda.empty_cache()
         result["decode_kv_share"] = decode_bench(args, "share")
+        torch.cuda.empty_cache()
+        result["decode_handoff"] = handoff_bench(args)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, W, H0, args.cpu_seq)
