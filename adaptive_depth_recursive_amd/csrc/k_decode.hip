@@ -93,6 +93,8 @@ __global__ __launch_bounds__(64) void k_dec_schedule(DecArgs a) {
     }
     req = -1;
   }
+  // the pages just pushed may be popped below by other lanes: make the stores visible first
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
   int top = top0 + tot_free;
 
   // admit queued requests into free slots, in slot order

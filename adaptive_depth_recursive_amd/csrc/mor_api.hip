@@ -1,6 +1,7 @@
-// Host runtime behind include/mor.h: config validation, workspace plan, weight packing and the
-// enqueue order of the MoR prefill. Host code only; every step of the computation runs in the
-// kernels of k_gemm.hip, k_attn.hip and k_route.hip.
+// Host runtime behind include/mor.h: config validation, workspace plan, weight packing, the
+// enqueue order of the MoR prefill and of a depth-wise batched decode iteration (replayed from a
+// captured graph). Host code only; every step of the computation runs in the kernels of
+// k_gemm_bf16.hip / k_gemm.hip, k_attn_bf16.hip / k_attn.hip, k_route.hip and k_decode.hip.
 //
 // Prefill order (MoR paper A.1-A.3; reading notes 1, 2.1-2.2, 3.1-3.2):
 //   first layer on all tokens -> router r=1
@@ -154,6 +155,9 @@ mor_status validate(const mor_config* c) {
     const int P = c->kv_page_tokens;
     if (P != 16 && P != 32 && P != 64 && P != 128) return fail(MOR_E_SHAPE, "kv_page_tokens must be 16, 32, 64 or 128");
     if (c->kv_pages < 0 || c->max_requests < 1) return fail(MOR_E_INVALID, "kv_pages >= 0, max_requests >= 1");
+    if (c->d_model > 4096) return fail(MOR_E_SHAPE, "decode supports d_model up to 4096");
+    if (((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim) % 32)
+      return fail(MOR_E_SHAPE, "decode needs (n_q_heads + 2 n_kv_heads) * head_dim % 32 == 0");
   }
   return MOR_OK;
 }

@@ -91,7 +91,8 @@ def test_null_handle_calls_rejected():
 
 
 @pytest.mark.parametrize("field,value", [
-    ("max_slots", 65), ("kv_page_tokens", 48), ("routing", 0), ("max_requests", 0), ("kv_pages", -1)])
+    ("max_slots", 65), ("kv_page_tokens", 48), ("routing", 0), ("max_requests", 0), ("kv_pages", -1),
+    ("d_model", 4160)])
 def test_invalid_decode_configs_rejected(field, value):
     mor = _lib()
     c = mor.make_config(workload.get_config("small_thr_bf16"), max_slots=5, kv_page_tokens=16,
