@@ -61,6 +61,9 @@ __device__ __forceinline__ float max2f(float a, float b) {
   return r;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.f, (__bf16)1.f};
+
 __device__ __forceinline__ bf16x8 rd(const char* base, int row, int chunk, int sw) {
   return *reinterpret_cast<const bf16x8*>(base + row * kRow + ((chunk ^ sw) << 4));
 }
@@ -71,8 +74,12 @@ template <int G>
 __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
   constexpr int BQ = 64, BKV = 64, HD = 64;
   constexpr int TILE = 2 * BKV * kRow;               // K tile + V^T tile
-  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE];
-  __shared__ int sKp[2][BKV];
+  // the two stages are separate LDS objects and the tile loop is unrolled by two, so the
+  // compiler can tell the prefetch into one stage from the reads of the other and does not wait
+  // for the prefetch before reading
+  __shared__ __attribute__((aligned(1024))) char smem0[TILE];
+  __shared__ __attribute__((aligned(1024))) char smem1[TILE];
+  __shared__ int sKp0[BKV], sKp1[BKV];
 
   const int b = blockIdx.y, kvh = blockIdx.z;
   const int qb = gridDim.x - 1 - blockIdx.x;         // longest blocks first
@@ -97,20 +104,30 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
   }
   const int kend = lo;
 
+  // Q is loaded once, pre-multiplied by scale * log2(e) and re-rounded to bf16, so that the
+  // S^T product comes out in base-2 exponent units.
+  const float sl2 = a.scale_log2;
   const bf16* Qb = reinterpret_cast<const bf16*>(a.q);
   bf16x8 qf[G][2];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      qf[hh][ks] = qvalid ? *reinterpret_cast<const bf16x8*>(Qb + (size_t)(off + qi) * a.ldq + (kvh * G + hh) * HD + ks * 32 + g * 8)
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 raw = qvalid ? *reinterpret_cast<const bf16x8*>(Qb + (size_t)(off + qi) * a.ldq + (kvh * G + hh) * HD + ks * 32 + g * 8)
                           : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) raw[e] = (bf16)((float)raw[e] * sl2);
+      qf[hh][ks] = raw;
+    }
 
-  float mrun[G], lrun[G];
+  // Per query (all four lanes that hold its column agree): reference maximum m in base-2 units,
+  // kept as the splat -m that seeds the S^T accumulators, so the product yields s * sl2 - m.
+  f32x4 nm4[G];
+  float lrun[G];
   f32x4 o[G][4];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    mrun[hh] = -INFINITY;
+    nm4[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
     lrun[hh] = 0.f;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) o[hh][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -119,24 +136,24 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
   const size_t ldk = (size_t)a.hkv * HD;
   const bf16* Kb = reinterpret_cast<const bf16*>(a.k) + (size_t)b * a.kpad * ldk + kvh * HD;
   const bf16* Vb = reinterpret_cast<const bf16*>(a.vt) + ((size_t)b * a.hkv + kvh) * HD * a.kpad;
-  auto issue = [&](int t0, int buf) {
-    char* st = smem + buf * TILE;
+  auto issue = [&](int t0, char* st, int* skp) {
     dma_rows<BKV>(Kb + (size_t)t0 * ldk, ldk, st, wave, lane, true);
     dma_rows<HD>(Vb + t0, a.kpad, st + BKV * kRow, wave, lane, false);
-    if (tid < BKV) sKp[buf][tid] = (t0 + tid < nk) ? kp[t0 + tid] : INT_MAX;
+    // key positions go the same way (global -> LDS, no register round trip, so nothing waits on
+    // them before the tile is needed); the index is clamped into the sequence, and keys at or
+    // beyond nk are masked by index in the tile that holds them
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds(kp + min(t0 + lane, nk - 1), (lds_void*)skp, 4, 0, 0);
   };
 
-  const float sl2 = a.scale_log2;
   const int ntiles = (kend + BKV - 1) / BKV;
-  if (ntiles > 0) issue(0, 0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int t0 = t * BKV, buf = t & 1;
+  // one key tile: wait for its stage, start the next tile's loads into the other stage, compute
+  auto step = [&](int t, const char* sk, const int* kps, char* nst, int* nkp) {
+    const int t0 = t * BKV;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < ntiles) issue(t0 + BKV, buf ^ 1);
-    const char* sk = smem + buf * TILE;
+    if (t + 1 < ntiles) issue(t0 + BKV, nst, nkp);
     const char* sv = sk + BKV * kRow;
-    const int* kps = sKp[buf];
     const bool need_mask = (t0 + BKV > nk) || (kps[BKV - 1] > wave_minpos);
 
     bf16x8 kf[4][2], vf[4][2];
@@ -156,68 +173,98 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
     // positions of this lane's 16 keys, for the tiles that need the causal mask
     int kpv[4][4];
     if (need_mask) {
+      const int lim = nk - t0 - 8 * g;                 // this lane's keys from index lim on are absent
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int4 p0 = *reinterpret_cast<const int4*>(&kps[32 * h2 + 8 * g]);
         const int4 p1 = *reinterpret_cast<const int4*>(&kps[32 * h2 + 8 * g + 4]);
         kpv[2 * h2][0] = p0.x; kpv[2 * h2][1] = p0.y; kpv[2 * h2][2] = p0.z; kpv[2 * h2][3] = p0.w;
         kpv[2 * h2 + 1][0] = p1.x; kpv[2 * h2 + 1][1] = p1.y; kpv[2 * h2 + 1][2] = p1.z; kpv[2 * h2 + 1][3] = p1.w;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (32 * h2 + 4 * hb + e >= lim) kpv[2 * h2 + hb][e] = INT_MAX;
       }
     }
 
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      // the four key blocks are independent: issue their first K halves, then their second
-      f32x4 s[4];
+    // S^T for one query head: the four key blocks are independent, so their first K halves are
+    // issued before their second
+    auto scores = [&](int hh, f32x4 (&s)[4]) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][0], qf[hh][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][0], qf[hh][0], nm4[hh], 0, 0, 0);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
         s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][1], qf[hh][1], s[kb], 0, 0, 0);
-      // s[kb][e] holds the raw score of key 32 (kb/2) + 8 g + 4 (kb & 1) + e of this tile
+    };
+    // Software pipeline over the query heads: the next head's S^T products are issued before
+    // this head's softmax, so the matrix cores work while the vector ALUs do.
+    f32x4 sc[4];
+    scores(0, sc);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      f32x4 s[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) s[kb] = sc[kb];
+      if (hh + 1 < G) scores(hh + 1, sc);
+      // s[kb][e]: scaled score of key 32 (kb/2) + 8 g + 4 (kb & 1) + e of this tile, minus m
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[kb][e] = kpv[kb][e] > myqpos ? -INFINITY : s[kb][e];
       }
-      float mraw = max3f(max3f(s[0][0], s[0][1], s[0][2]), max3f(s[0][3], s[1][0], s[1][1]),
-                         max3f(s[1][2], s[1][3], s[2][0]));
-      mraw = max3f(mraw, max3f(s[2][1], s[2][2], s[2][3]), max3f(s[3][0], s[3][1], s[3][2]));
-      mraw = max2f(mraw, s[3][3]);
-      mraw = max2f(mraw, __shfl_xor(mraw, 16));
-      mraw = max2f(mraw, __shfl_xor(mraw, 32));
-      const float mloc = mraw * sl2;                   // scores enter the exponent scaled by sl2
-      if (__any(mloc > mrun[hh] + 8.f)) {              // raise the reference maximum, rescale
-        const float mnew = fmaxf(mrun[hh], mloc);
-        const float alpha = __builtin_amdgcn_exp2f(mrun[hh] - mnew);
-        lrun[hh] *= alpha;
+      float mx = max3f(max3f(s[0][0], s[0][1], s[0][2]), max3f(s[0][3], s[1][0], s[1][1]),
+                       max3f(s[1][2], s[1][3], s[2][0]));
+      mx = max3f(mx, max3f(s[2][1], s[2][2], s[2][3]), max3f(s[3][0], s[3][1], s[3][2]));
+      mx = max2f(mx, s[3][3]);
+      // m is raised (and O, l rescaled) only on the first tile or when a score exceeds it by
+      // more than 2^8; the vote is wave-wide, the new m is agreed within each query's lanes.
+      if (t == 0 || __any(mx > 8.f)) {
+        mx = max2f(mx, __shfl_xor(mx, 16));
+        mx = max2f(mx, __shfl_xor(mx, 32));
+        const float shift = t == 0 ? mx : fmaxf(mx, 0.f);
+        if (t > 0) {
+          const float alpha = __builtin_amdgcn_exp2f(-shift);
+          lrun[hh] *= alpha;
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) o[hh][hb] *= alpha;
-        mrun[hh] = mnew;
+          for (int hb = 0; hb < 4; ++hb) o[hh][hb] *= alpha;
+        }
+        const float nm = nm4[hh][0] - shift;
+        nm4[hh] = f32x4{nm, nm, nm, nm};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[kb][e] -= shift;
       }
-      const float nm = -mrun[hh];
-      float pr[4][4];
       bf16x8 pf[2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pr[kb][e] = __builtin_amdgcn_exp2f(fmaf(s[kb][e], sl2, nm));
-          pf[kb >> 1][4 * (kb & 1) + e] = (bf16)pr[kb][e];
-        }
-      // row sum as a tree (short dependency chains)
-      float ls[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) ls[kb] = (pr[kb][0] + pr[kb][1]) + (pr[kb][2] + pr[kb][3]);
-      lrun[hh] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        for (int e = 0; e < 4; ++e) pf[kb >> 1][4 * (kb & 1) + e] = (bf16)__builtin_amdgcn_exp2f(s[kb][e]);
+      // row sum of the bf16 probabilities the PV product uses: two-term dot products with
+      // (1, 1), in two chains
+      float l0 = lrun[hh], l1 = 0.f;
+#define MOR_PAIR_SUM(j)                                                                       \
+  l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[0], pf[0], 2 * j, 2 * j + 1), \
+                                       kOnes2, l0, false);                                    \
+  l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[1], pf[1], 2 * j, 2 * j + 1), \
+                                       kOnes2, l1, false);
+      MOR_PAIR_SUM(0) MOR_PAIR_SUM(1) MOR_PAIR_SUM(2) MOR_PAIR_SUM(3)
+#undef MOR_PAIR_SUM
+      lrun[hh] = l0 + l1;
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb)
           o[hh][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[hb][k2], pf[k2], o[hh][hb], 0, 0, 0);
     }
+  };
+  if (ntiles > 0) issue(0, smem0, sKp0);
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, smem0, sKp0, smem1, sKp1);
+    if (t + 1 < ntiles) step(t + 1, smem1, sKp1, smem0, sKp0);
   }
 
   if (!qvalid) return;
