@@ -81,8 +81,23 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem1[TILE];
   __shared__ int sKp0[BKV], sKp1[BKV];
 
-  const int b = blockIdx.y, kvh = blockIdx.z;
-  const int qb = gridDim.x - 1 - blockIdx.x;         // longest blocks first
+  // Workgroups are dealt round-robin over the 8 XCDs by linear id. When the (sequence, KV head)
+  // pairs split evenly over the XCDs, each XCD gets its own pairs (their K/V then stay in that
+  // XCD's L2) and takes their query blocks longest first; otherwise the grid order is used.
+  const int nqb = gridDim.x, npair = gridDim.y * gridDim.z;
+  int b, kvh, qb;
+  if (npair % 8 == 0) {
+    const int lin = blockIdx.x + nqb * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int ppx = npair / 8, slot = lin >> 3;
+    const int pair = (lin & 7) * ppx + slot % ppx;
+    b = pair % gridDim.y;
+    kvh = pair / gridDim.y;
+    qb = nqb - 1 - slot / ppx;
+  } else {
+    b = blockIdx.y;
+    kvh = blockIdx.z;
+    qb = nqb - 1 - blockIdx.x;                       // longest blocks first
+  }
   const int nq = a.qcnt[b];
   if (qb * BQ >= nq) return;
   const int nk = a.kcnt[b];
