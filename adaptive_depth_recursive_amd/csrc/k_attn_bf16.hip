@@ -112,12 +112,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
   const int wave_minpos = wq0 < nq ? a.qpos[off + wq0] : INT_MAX;
   const int maxpos = a.qpos[off + min(qb * BQ + BQ - 1, nq - 1)];
   const int* kp = a.kpos + (size_t)b * a.ldkpos;
-  int lo = 0, hi = nk;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (kp[mid] <= maxpos) lo = mid + 1; else hi = mid;
-  }
-  const int kend = lo;
+  const size_t ldk = (size_t)a.hkv * HD;
+  const bf16* Kb = reinterpret_cast<const bf16*>(a.k) + (size_t)b * a.kpad * ldk + kvh * HD;
+  const bf16* Vb = reinterpret_cast<const bf16*>(a.vt) + ((size_t)b * a.hkv + kvh) * HD * a.kpad;
+  auto issue = [&](int t0, char* st, int* skp) {
+    dma_rows<BKV>(Kb + (size_t)t0 * ldk, ldk, st, wave, lane, true);
+    dma_rows<HD>(Vb + t0, a.kpad, st + BKV * kRow, wave, lane, false);
+    // key positions go the same way (global -> LDS, no register round trip, so nothing waits on
+    // them before the tile is needed); the index is clamped into the sequence, and keys at or
+    // beyond nk are masked by index in the tile that holds them
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds(kp + min(t0 + lane, nk - 1), (lds_void*)skp, 4, 0, 0);
+  };
 
   // Q is loaded once, pre-multiplied by scale * log2(e) and re-rounded to bf16, so that the
   // S^T product comes out in base-2 exponent units.
@@ -127,13 +133,32 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 raw = qvalid ? *reinterpret_cast<const bf16x8*>(Qb + (size_t)(off + qi) * a.ldq + (kvh * G + hh) * HD + ks * 32 + g * 8)
+    for (int ks = 0; ks < 2; ++ks)
+      qf[hh][ks] = qvalid ? *reinterpret_cast<const bf16x8*>(Qb + (size_t)(off + qi) * a.ldq + (kvh * G + hh) * HD + ks * 32 + g * 8)
                           : bf16x8{};
+
+  // Every query sees the first key tile, so its loads start before the key range is known.
+  if (nk > 0) issue(0, smem0, sKp0);
+  // kend = number of keys with position <= maxpos (positions ascend): each round samples the
+  // remaining range at 64 evenly spaced keys, one per lane, and keeps the gap the count falls
+  // in, so a few dependent loads replace a binary search's log2(nk)
+  int lo = 0, hi = nk;
+  while (hi - lo > 64) {
+    const int stride = (hi - lo + 63) / 64;
+    const int i = lo + lane * stride;
+    const int c = __popcll(__ballot(i < hi && kp[i] <= maxpos));
+    if (c == 0) { hi = lo; break; }
+    hi = min(hi, lo + c * stride);
+    lo += (c - 1) * stride + 1;
+  }
+  const int kend = lo + __popcll(__ballot(lo + lane < hi && kp[lo + lane] <= maxpos));
+
 #pragma unroll
-      for (int e = 0; e < 8; ++e) raw[e] = (bf16)((float)raw[e] * sl2);
-      qf[hh][ks] = raw;
-    }
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[hh][ks][e] = (bf16)((float)qf[hh][ks][e] * sl2);
 
   // Per query (all four lanes that hold its column agree): reference maximum m in base-2 units,
   // kept as the splat -m that seeds the S^T accumulators, so the product yields s * sl2 - m.
@@ -148,20 +173,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
     for (int hb = 0; hb < 4; ++hb) o[hh][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const size_t ldk = (size_t)a.hkv * HD;
-  const bf16* Kb = reinterpret_cast<const bf16*>(a.k) + (size_t)b * a.kpad * ldk + kvh * HD;
-  const bf16* Vb = reinterpret_cast<const bf16*>(a.vt) + ((size_t)b * a.hkv + kvh) * HD * a.kpad;
-  auto issue = [&](int t0, char* st, int* skp) {
-    dma_rows<BKV>(Kb + (size_t)t0 * ldk, ldk, st, wave, lane, true);
-    dma_rows<HD>(Vb + t0, a.kpad, st + BKV * kRow, wave, lane, false);
-    // key positions go the same way (global -> LDS, no register round trip, so nothing waits on
-    // them before the tile is needed); the index is clamped into the sequence, and keys at or
-    // beyond nk are masked by index in the tile that holds them
-    if (wave == 0)
-      __builtin_amdgcn_global_load_lds(kp + min(t0 + lane, nk - 1), (lds_void*)skp, 4, 0, 0);
-  };
+
 
   const int ntiles = (kend + BKV - 1) / BKV;
+  if (ntiles == 0 && nk > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain tile 0
   // one key tile: wait for its stage, start the next tile's loads into the other stage, compute
   auto step = [&](int t, const char* sk, const int* kps, char* nst, int* nkp) {
     const int t0 = t * BKV;
@@ -276,7 +291,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
           o[hh][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[hb][k2], pf[k2], o[hh][hb], 0, 0, 0);
     }
   };
-  if (ntiles > 0) issue(0, smem0, sKp0);
   for (int t = 0; t < ntiles; t += 2) {
     step(t, smem0, sKp0, smem1, sKp1);
     if (t + 1 < ntiles) step(t + 1, smem1, sKp1, smem0, sKp0);
