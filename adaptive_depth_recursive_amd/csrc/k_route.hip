@@ -337,7 +337,7 @@ hipError_t launch_scatter(float* H, const float* X, int d, const int* meta, int 
 
 // ------------------------------------------------------------------ RMSNorm
 // One wave per row: Xn = X / sqrt(mean(X^2) + eps) * g, rounded to the GEMM input type.
-template <typename T>
+template <typename T, int CH>
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ X, int d,
                                                  const int* __restrict__ meta,
                                                  const float* __restrict__ g, float eps,
@@ -347,18 +347,42 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ X, in
   if (i >= meta[0]) return;
   const float4* x = reinterpret_cast<const float4*>(X + (size_t)i * d);
   const float4* g4 = reinterpret_cast<const float4*>(g);
-  float ss = 0.f;
-  for (int c = lane; c < d / 4; c += WAVE) {
-    const float4 v = x[c];
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  ss = wave_sum(ss);
-  const float rinv = 1.f / sqrtf(ss / (float)d + eps);
   T* out = Xn + (size_t)i * d;
-  for (int c = lane; c < d / 4; c += WAVE) {
-    const float4 v = x[c], gg = g4[c];
-    Vec4<T>::store(out + 4 * c, v.x * rinv * gg.x, v.y * rinv * gg.y, v.z * rinv * gg.z,
-                   v.w * rinv * gg.w);
+  const int n4 = d / 4;
+  if constexpr (CH > 0) {
+    // the row stays in registers (CH float4 per lane): one read of X
+    float4 v[CH];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int c = lane + k * WAVE;
+      v[k] = c < n4 ? x[c] : float4{0.f, 0.f, 0.f, 0.f};
+      ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+    }
+    ss = wave_sum(ss);
+    const float rinv = 1.f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int c = lane + k * WAVE;
+      if (c < n4) {
+        const float4 gg = g4[c];
+        Vec4<T>::store(out + 4 * c, v[k].x * rinv * gg.x, v[k].y * rinv * gg.y, v[k].z * rinv * gg.z,
+                       v[k].w * rinv * gg.w);
+      }
+    }
+  } else {
+    float ss = 0.f;
+    for (int c = lane; c < n4; c += WAVE) {
+      const float4 v = x[c];
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    const float rinv = 1.f / sqrtf(ss / (float)d + eps);
+    for (int c = lane; c < n4; c += WAVE) {
+      const float4 v = x[c], gg = g4[c];
+      Vec4<T>::store(out + 4 * c, v.x * rinv * gg.x, v.y * rinv * gg.y, v.z * rinv * gg.z,
+                     v.w * rinv * gg.w);
+    }
   }
 }
 
@@ -366,7 +390,11 @@ template <typename T>
 hipError_t launch_rmsnorm(const float* X, int d, const int* meta, int m_upper, const float* g,
                           float eps, T* Xn, hipStream_t s) {
   if (m_upper <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_rmsnorm<T>), dim3((m_upper + 3) / 4), dim3(256), 0, s, X, d, meta, g, eps, Xn);
+  const dim3 grid((m_upper + 3) / 4);
+  if (d <= 4 * 4 * WAVE)
+    hipLaunchKernelGGL((k_rmsnorm<T, 4>), grid, dim3(256), 0, s, X, d, meta, g, eps, Xn);
+  else
+    hipLaunchKernelGGL((k_rmsnorm<T, 0>), grid, dim3(256), 0, s, X, d, meta, g, eps, Xn);
   return hipGetLastError();
 }
 template hipError_t launch_rmsnorm<float>(const float*, int, const int*, int, const float*, float, float*, hipStream_t);
