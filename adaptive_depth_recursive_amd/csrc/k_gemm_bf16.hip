@@ -28,21 +28,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// Issue the loads of `rows` rows starting at global row `g0` (clamped to last_row) into the
-// LDS region `dst` (row-major, swizzled). Rows are split over the 4 waves, 8 per instruction.
-template <int ROWS>
-__device__ __forceinline__ void load_rows(const bf16* __restrict__ src, int ld, int g0,
-                                          int last_row, int k0, char* dst, int wave, int lane) {
-  constexpr int INSTR = ROWS / 8 / 4;             // instructions per wave
+// Issue one stage's loads of NI wave instructions for one operand: instruction i moves the 8
+// rows starting at (4 i + wave) * 8, each lane its 16-byte chunk at element offset off[i] from
+// `base`.
+template <int NI>
+__device__ __forceinline__ void load_stage(const bf16* base, const int* off, char* dst, int wave) {
 #pragma unroll
-  for (int i = 0; i < INSTR; ++i) {
-    const int rb = (i * 4 + wave) * 8;            // first row of this wave instruction
-    const int r = rb + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);            // global 16-byte chunk that lands at slot lane&7
-    const int gr = min(g0 + r, last_row);
-    const bf16* gp = src + (size_t)gr * ld + k0 + c * 8;
-    __builtin_amdgcn_global_load_lds(gp, (lds_void*)(dst + rb * kRowBytes), 16, 0, 0);
-  }
+  for (int i = 0; i < NI; ++i)
+    __builtin_amdgcn_global_load_lds(base + off[i], (lds_void*)(dst + (i * 4 + wave) * 8 * kRowBytes), 16, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 frag(const char* base, int row, int chunk) {
@@ -90,12 +83,31 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(const bf16* __restrict__ A
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / 64;
+  // Operand tiles move global -> LDS with global_load_lds_dwordx4: one wave instruction writes
+  // 1 KB = 8 rows x 128 bytes, contiguous in LDS; lane l loads the global 16-byte chunk that
+  // lands at slot l & 7 of its row. The per-lane element offsets (from the tile's first row,
+  // rows clamped into the operand) are computed once; a stage only adds its K offset.
+  constexpr int IW = BN / 32, IA = BM / 32;       // load instructions per wave per stage
+  const bf16* Wt = W + (size_t)n0 * K;
+  const bf16* At = A + (size_t)m0 * K;
+  int offw[IW], offa[IA];
+#pragma unroll
+  for (int i = 0; i < IW; ++i) {
+    const int r = (i * 4 + wave) * 8 + (lane >> 3);
+    offw[i] = min(r, N - 1 - n0) * K + ((lane & 7) ^ swz(r)) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < IA; ++i) {
+    const int r = (i * 4 + wave) * 8 + (lane >> 3);
+    offa[i] = min(r, M - 1 - m0) * K + ((lane & 7) ^ swz(r)) * 8;
+  }
   auto issue = [&](int kt, int buf) {
     char* st = smem + buf * STAGE;
-    load_rows<BN>(W, K, n0, N - 1, kt * 64, st, wave, lane);
-    load_rows<BM>(A, K, m0, M - 1, kt * 64, st + BN * kRowBytes, wave, lane);
+    load_stage<IW>(Wt + kt * 64, offw, st, wave);
+    load_stage<IA>(At + kt * 64, offa, st + BN * kRowBytes, wave);
   };
+
+  const int nk = K / 64;
   issue(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -103,19 +115,32 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(const bf16* __restrict__ A
     if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
     const char* sw = smem + (kt & 1) * STAGE;
     const char* sa = sw + BN * kRowBytes;
+    // both 32-deep halves' fragments are requested up front: the second half's reads are in
+    // flight while the first half multiplies
+    bf16x8 a[2][FN], b[2][FM];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 a[FN], b[FM];
 #pragma unroll
-      for (int i = 0; i < FN; ++i) a[i] = frag(sw, wn * WN + i * 16 + fr, ks * 4 + g);
+      for (int i = 0; i < FN; ++i) a[ks][i] = frag(sw, wn * WN + i * 16 + fr, ks * 4 + g);
 #pragma unroll
-      for (int j = 0; j < FM; ++j) b[j] = frag(sa, wm * WM + j * 16 + fr, ks * 4 + g);
+      for (int j = 0; j < FM; ++j) b[ks][j] = frag(sa, wm * WM + j * 16 + fr, ks * 4 + g);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
+    // keep that order through scheduling: the first half's reads, then its matrix ops with the
+    // second half's reads spread between them, then the second half's matrix ops
+    __builtin_amdgcn_sched_group_barrier(0x100, FN + FM, 0);
+#pragma unroll
+    for (int r = 0; r < FN + FM; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, FN * FM / (FN + FM), 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, FN * FM, 0);
   }
 
   // ------------------------------------------------------------------ epilogues
