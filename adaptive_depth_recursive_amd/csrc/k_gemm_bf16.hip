@@ -107,12 +107,32 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(const bf16* __restrict__ A
     load_stage<IA>(At + kt * 64, offa, st + BN * kRowBytes, wave);
   };
 
+  const int g4 = g * 4;
+  const int nw = n0 + wn * WN;
+  const int mw = m0 + wm * WM + fr;
+  // residual epilogue of the 128 x 128 tile: the stream values this lane updates are loaded
+  // during the last stage's matrix ops (no stage loads are in flight then), not after them
+  constexpr bool kPrefetchX = EPI == EPI_RESID && BN * BM <= 128 * 128;
+  float4 xr[kPrefetchX ? FN : 1][kPrefetchX ? FM : 1];
+
   const int nk = K / 64;
   issue(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+    if constexpr (kPrefetchX) {
+      if (kt + 1 == nk) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+          for (int i = 0; i < FN; ++i) {
+            const int m = mw + 16 * j, n = nw + 16 * i + g4;
+            xr[i][j] = (m < M && n < N) ? *reinterpret_cast<const float4*>(ep.x + (size_t)m * ep.ldx + n)
+                                        : float4{0.f, 0.f, 0.f, 0.f};
+          }
+      }
+    }
     const char* sw = smem + (kt & 1) * STAGE;
     const char* sa = sw + BN * kRowBytes;
     // both 32-deep halves' fragments are requested up front: the second half's reads are in
@@ -144,9 +164,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(const bf16* __restrict__ A
   }
 
   // ------------------------------------------------------------------ epilogues
-  const int g4 = g * 4;
-  const int nw = n0 + wn * WN;
-  const int mw = m0 + wm * WM + fr;
   if constexpr (EPI == EPI_RESID) {
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
@@ -156,10 +173,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(const bf16* __restrict__ A
       for (int i = 0; i < FN; ++i) {
         const int n = nw + 16 * i + g4;
         if (n >= N) continue;
-        float4* px = reinterpret_cast<float4*>(ep.x + (size_t)m * ep.ldx + n);
-        float4 v = *px;
+        float4 v;
+        if constexpr (kPrefetchX) v = xr[i][j];
+        else v = *reinterpret_cast<const float4*>(ep.x + (size_t)m * ep.ldx + n);
         v.x += acc[i][j][0]; v.y += acc[i][j][1]; v.z += acc[i][j][2]; v.w += acc[i][j][3];
-        *px = v;
+        *reinterpret_cast<float4*>(ep.x + (size_t)m * ep.ldx + n) = v;
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
