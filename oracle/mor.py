@@ -42,7 +42,7 @@ __all__ = [
     "bf16_round", "layer_map", "recursion_of_layer", "capacity_counts", "rmsnorm",
     "rope", "attention", "block", "router_logits_fp32", "sigmoid", "select_topk",
     "prefill", "threshold_forward", "decode_sequence", "kv_entries", "to_f64_weights",
-    "calibrate_threshold_bias",
+    "calibrate_threshold_bias", "shared_schedule",
 ]
 
 
@@ -252,9 +252,9 @@ def select_topk(active_pos: np.ndarray, z: np.ndarray, k: int) -> np.ndarray:
 # ----------------------------------------------------------------------------- forward
 def to_f64_weights(weights: dict) -> dict:
     def lay(L):
-        return {k: np.asarray(v, np.float64) for k, v in L.items()}
-    return {"first": lay(weights["first"]), "shared": [lay(s) for s in weights["shared"]],
-            "last": lay(weights["last"]),
+        return None if L is None else {k: np.asarray(v, np.float64) for k, v in L.items()}
+    return {"first": lay(weights.get("first")), "shared": [lay(s) for s in weights["shared"]],
+            "last": lay(weights.get("last")),
             "router_w": np.asarray(weights["router_w"], np.float32),
             "router_b": np.asarray(weights.get("router_b", np.zeros(len(weights["router_w"]))),
                                    np.float32)}
@@ -265,11 +265,36 @@ def _softmax(z):
     return e / e.sum(axis=-1, keepdims=True)
 
 
+def shared_schedule(cfg) -> List[List[int]]:
+    """Index into the shared pool of the layer at (recursion r, position j), as [r-1][j-1].
+
+    The routed recursions are consecutive spans of n_s unrolled layers (after the unique
+    first layer under Middle-* sharing); the layer-to-block map of the sharing scheme
+    ([Notes] section 1, [MoR] Appendix A.1, see layer_map) decides which block each
+    unrolled layer of a span uses. Under Cycle and Middle-Cycle position j always uses
+    block j; under Sequence and Middle-Sequence consecutive layers repeat a block N_r times.
+    """
+    scheme = getattr(cfg, "sharing", "middle_cycle")
+    R, L = cfg.n_rec, cfg.n_layers
+    lm = layer_map(L, R, scheme)
+    middle = scheme.startswith("middle")
+    mid = lm[1:-1] if middle else lm
+    n_s = len(mid) // R
+    base = 1 if middle else 0                       # layer_map numbers the pool from 1 under Middle-*
+    return [[mid[(r - 1) * n_s + (j - 1)] - base for j in range(1, n_s + 1)]
+            for r in range(1, R + 1)]
+
+
 def _prefill_one(cfg, W, h0, ks, forced, gate_mode, update):
     T = h0.shape[0]
     pos_all = np.arange(T)
     R, n_s = cfg.n_rec, cfg.n_shared
-    H, kv_first = block(W["first"], h0, pos_all, cfg)
+    sched = shared_schedule(cfg)
+    middle = getattr(cfg, "sharing", "middle_cycle").startswith("middle")
+    if middle:
+        H, kv_first = block(W["first"], h0, pos_all, cfg)
+    else:                                           # Cycle / Sequence: no unique entry layer
+        H, kv_first = np.array(h0, np.float64), None
     hist = [H.copy()]
     kv = {"first": kv_first}
     rec1 = {}
@@ -310,10 +335,12 @@ def _prefill_one(cfg, W, h0, ks, forced, gate_mode, update):
             raise ValueError(cfg.routing)
         X = H[sel]
         for j in range(1, n_s + 1):
+            Wj = W["shared"][sched[r - 1][j - 1]]
             if cfg.kv_mode == "share" and r >= 2:
-                X, _ = block(W["shared"][j - 1], X, sel, cfg, kv_src=rec1[j])
+                # recursive KV sharing reuses the recursion-1 keys of the same position j
+                X, _ = block(Wj, X, sel, cfg, kv_src=rec1[j])
             else:
-                X, kvj = block(W["shared"][j - 1], X, sel, cfg)
+                X, kvj = block(Wj, X, sel, cfg)
                 kv[(r, j)] = kvj
                 if r == 1:
                     rec1[j] = kvj
@@ -338,7 +365,10 @@ def _prefill_one(cfg, W, h0, ks, forced, gate_mode, update):
         sel_list.append(np.asarray(sel))
         g_list.append(g)
         active = np.asarray(sel)
-    out, kv_last = block(W["last"], H, pos_all, cfg)
+    if middle:
+        out, kv_last = block(W["last"], H, pos_all, cfg)
+    else:                                           # Cycle / Sequence: no unique exit layer
+        out, kv_last = H.copy(), None
     kv["last"] = kv_last
     res = {"out": out, "sel": sel_list, "own_sel": own_list, "z": z_list, "gate": g_list,
            "hist": hist, "kv": kv}
@@ -352,7 +382,8 @@ def prefill(cfg, weights, H0: np.ndarray, forced_sel=None, gate_mode: Optional[s
             update: str = "delta", keep_kv: bool = False) -> dict:
     """MoR prefill over a batch, one sequence at a time (sequences are independent).
 
-    [Notes] sections 1 and 2.1, [MoR] Appendix A: Middle-Cycle unrolling; at recursion r
+    [Notes] sections 1 and 2.1, [MoR] Appendix A: the configured sharing scheme's unrolling
+    (Middle-Cycle by default; see shared_schedule); at recursion r
     the router scores the tokens active at r-1, keeps ceil(cap_r * T) of them (expert
     choice), runs the n_s shared layers on them with attention restricted to tokens
     active at r (recursion-wise caching, [Notes] 3.1) or to the recursion-1 keys
@@ -404,6 +435,8 @@ def decode_sequence(cfg, weights, inputs: np.ndarray, gate_mode: Optional[str] =
     (r, layer) (or to the recursion-1 cache under KV sharing), then the last layer.
     Returns outputs [n, d] and exit depths [n].
     """
+    if getattr(cfg, "sharing", "middle_cycle") != "middle_cycle":
+        raise ValueError("depth-wise decode is defined for Middle-Cycle sharing")
     W = to_f64_weights(weights)
     gm = gate_mode or cfg.gate_mode
     R, n_s, d = cfg.n_rec, cfg.n_shared, cfg.d_model

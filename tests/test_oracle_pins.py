@@ -224,6 +224,48 @@ def test_full_capacity_bitwise_against_unrolled_loop():
     assert np.array_equal(res["out"][0], X)
 
 
+def test_shared_schedule_follows_printed_maps():
+    """The (recursion, position) -> shared-block schedule is the printed unrolling, span by span."""
+    for ex in _gold("sharing_examples.json")["examples"]:
+        cfg = workload.get_config("small_f32", n_layers=ex["n_layers"], n_rec=ex["n_rec"],
+                                  sharing=ex["scheme"])
+        sched = oracle.shared_schedule(cfg)
+        middle = ex["scheme"].startswith("middle")
+        printed = ex["blocks"][1:-1] if middle else ex["blocks"]
+        flat = [b + (1 if middle else 0) for span in sched for b in span]
+        assert flat == printed, ex
+        assert len(sched) == ex["n_rec"] and all(len(sp) == cfg.n_shared for sp in sched)
+
+
+@pytest.mark.parametrize("scheme,L", [("middle_cycle", 8), ("middle_sequence", 8), ("cycle", 9),
+                                      ("sequence", 9)])
+def test_full_capacity_each_sharing_scheme_is_its_unrolled_stack(scheme, L):
+    """Capacities all 1 with unit gating, under every sharing scheme: MoR equals a plain Llama stack
+    whose layers follow that scheme's map ([Notes] section 1; transformers, float64)."""
+    cfg = _unit_cfg("small_f32", cap_num=(3, 3, 3), cap_den=3, seq=31, batch=2, n_layers=L,
+                    sharing=scheme)
+    W = workload.make_weights(cfg)
+    H0 = workload.make_inputs(cfg)
+    res = oracle.prefill(cfg, W, H0)
+    if cfg.middle:
+        layers = [W["first"]] + W["shared"] + [W["last"]]
+    else:
+        assert W["first"] is None and W["last"] is None
+        layers = W["shared"]
+    ref = llama_stack(cfg, layers, oracle.layer_map(cfg.n_layers, cfg.n_rec, scheme), H0)
+    assert np.allclose(res["out"], ref, rtol=HF_RTOL, atol=HF_ATOL)
+
+
+def test_schemes_differ_when_the_pool_is_not_trivial():
+    """Middle-Cycle and Middle-Sequence share weights and inputs but not the layer order, so their
+    outputs differ (a scheme argument that were ignored would make them equal)."""
+    a = _unit_cfg("small_f32", cap_num=(3, 3, 3), cap_den=3, seq=19, batch=1)
+    b = a.replace(sharing="middle_sequence")
+    W = workload.make_weights(a)
+    H0 = workload.make_inputs(a)
+    assert not np.allclose(oracle.prefill(a, W, H0)["out"], oracle.prefill(b, W, H0)["out"])
+
+
 def test_bf16_block_close_to_fp64_llama():
     """The bf16 storage points perturb a layer by bf16 rounding only (relative error ~1e-2 at most)."""
     cfg = workload.get_config("small_bf16", n_layers=2 + 3, n_rec=3, seq=50, batch=1, gate_mode="unit",

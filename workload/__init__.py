@@ -55,6 +55,7 @@ class MorConfig:
     routing: str = "ec"        # "ec" | "tc" | "threshold"
     kv_mode: str = "recursion" # "recursion" | "share"
     gate_mode: str = "router"  # "router" | "unit"
+    sharing: str = "middle_cycle"  # "middle_cycle" | "middle_sequence" | "cycle" | "sequence"
     rms_eps: float = 1e-5
     rope_theta: float = 10000.0
     # decode-only fields
@@ -67,8 +68,14 @@ class MorConfig:
         return dataclasses.replace(self, **kw)
 
     @property
+    def middle(self) -> bool:
+        """Middle-* sharing: unique first and last layers around the recursions."""
+        return self.sharing.startswith("middle")
+
+    @property
     def n_shared(self) -> int:
-        return (self.n_layers - 2) // self.n_rec
+        """Layers per recursion (= size of the shared block pool)."""
+        return ((self.n_layers - 2) if self.middle else self.n_layers) // self.n_rec
 
 
 def _c(name, **kw) -> MorConfig:
@@ -158,9 +165,13 @@ def layer_shapes(cfg: MorConfig) -> Dict[str, Tuple[int, int]]:
 def make_weights(cfg: MorConfig, seed: int = SEED_WEIGHTS) -> Dict[str, object]:
     """Draw all weights. Returns {"first": layer, "shared": [layer]*n_s, "last": layer,
     "router_w": [N_r][d] float32, "router_b": [N_r] float32}; a layer is a dict of
-    [out][in] float32 arrays plus "g_attn"/"g_ffn" gains (ones)."""
-    if (cfg.n_layers - 2) % cfg.n_rec != 0:
-        raise ValueError("n_layers - 2 must be divisible by n_rec")
+    [out][in] float32 arrays plus "g_attn"/"g_ffn" gains (ones). Under Cycle and Sequence
+    sharing there are no unique layers: "first" and "last" are None and are not drawn."""
+    span = cfg.n_layers - 2 if cfg.middle else cfg.n_layers
+    if cfg.sharing not in ("middle_cycle", "middle_sequence", "cycle", "sequence"):
+        raise ValueError(cfg.sharing)
+    if span % cfg.n_rec != 0 or span < cfg.n_rec:
+        raise ValueError("the shared span of layers must be a positive multiple of n_rec")
     rng = np.random.Generator(np.random.PCG64(seed))
     shapes = layer_shapes(cfg)
 
@@ -171,9 +182,9 @@ def make_weights(cfg: MorConfig, seed: int = SEED_WEIGHTS) -> Dict[str, object]:
         lay["g_ffn"] = np.ones(cfg.d_model, np.float32)
         return lay
 
-    first = draw_layer()
+    first = draw_layer() if cfg.middle else None
     shared = [draw_layer() for _ in range(cfg.n_shared)]
-    last = draw_layer()
+    last = draw_layer() if cfg.middle else None
     if cfg.routing == "tc":
         std = 2.0 / np.sqrt(cfg.d_model)
     else:
