@@ -21,6 +21,7 @@ MOR_F32, MOR_BF16 = 0, 1
 ROUTING = {"ec": 0, "tc": 1, "threshold": 2}
 KV_MODE = {"recursion": 0, "share": 1}
 GATE_MODE = {"router": 0, "unit": 1}
+SHARING = {"middle_cycle": 0, "middle_sequence": 1, "cycle": 2, "sequence": 3}
 DTYPE = {"f32": MOR_F32, "bf16": MOR_BF16}
 
 
@@ -41,6 +42,7 @@ class mor_config(ctypes.Structure):
         ("max_batch", ctypes.c_int32), ("max_seq", ctypes.c_int32),
         ("max_slots", ctypes.c_int32), ("kv_page_tokens", ctypes.c_int32),
         ("kv_pages", ctypes.c_int32), ("max_requests", ctypes.c_int32),
+        ("sharing", ctypes.c_int32),
     ]
 
 
@@ -131,7 +133,52 @@ def make_config(cfg, max_batch: Optional[int] = None, max_seq: Optional[int] = N
     c.max_seq = cfg.seq if max_seq is None else max_seq
     c.max_slots, c.kv_page_tokens = max_slots, kv_page_tokens
     c.kv_pages, c.max_requests = kv_pages, max_requests
+    c.sharing = SHARING[getattr(cfg, "sharing", "middle_cycle")]
     return c
+
+
+def extend_recursions(cfg, weights: Dict, extra: int = 1, cap_num=None, router_w=None,
+                      router_b=None):
+    """Test-time recursion scaling (MoR's depth is a runtime parameter: the same shared blocks can
+    be unrolled further at inference, without retraining).
+
+    Returns (cfg', weights') that run N_r + extra recursions over the same pool of n_s shared
+    blocks: n_rec and n_layers grow by `extra` spans of n_s layers. Only the cycle-type schemes
+    (middle_cycle, cycle) keep every block's place when the depth grows, so only they are
+    accepted. The extra steps' capacities (numerators over cap_den) default to the last trained
+    capacity; their router rows and biases default to the last trained ones.
+    cfg must be a dataclass with the workload configuration's fields.
+    """
+    import dataclasses
+
+    import numpy as np
+    if extra < 1:
+        raise ValueError("extra must be >= 1")
+    sharing = getattr(cfg, "sharing", "middle_cycle")
+    if sharing not in ("middle_cycle", "cycle"):
+        raise ValueError("test-time recursion scaling needs cycle-type sharing")
+    R = cfg.n_rec + extra
+    if R > MOR_MAX_REC:
+        raise ValueError(f"at most {MOR_MAX_REC} recursions")
+    n_s = cfg.n_shared
+    caps = tuple(cfg.cap_num[:cfg.n_rec]) + (
+        tuple(cap_num) if cap_num is not None else (cfg.cap_num[cfg.n_rec - 1],) * extra)
+    if len(caps) != R:
+        raise ValueError("cap_num must give one capacity per extra recursion")
+    L = R * n_s + (2 if sharing == "middle_cycle" else 0)
+    cfg2 = dataclasses.replace(cfg, n_rec=R, n_layers=L, cap_num=caps)
+    rw = np.asarray(weights["router_w"], np.float32)
+    add_w = (np.repeat(rw[-1:], extra, axis=0) if router_w is None
+             else np.asarray(router_w, np.float32).reshape(extra, -1))
+    w2 = dict(weights)
+    w2["router_w"] = np.concatenate([rw, add_w])
+    rb = weights.get("router_b")
+    if rb is not None or router_b is not None:
+        rb = np.zeros(cfg.n_rec, np.float32) if rb is None else np.asarray(rb, np.float32)
+        add_b = (np.repeat(rb[-1:], extra) if router_b is None
+                 else np.asarray(router_b, np.float32).reshape(extra))
+        w2["router_b"] = np.concatenate([rb, add_b])
+    return cfg2, w2
 
 
 def workspace_bytes(c: mor_config) -> int:
@@ -155,7 +202,8 @@ class Mor:
     """One initialised library handle with its device weights and workspace (torch tensors).
 
     weights: {"first": layer, "shared": [layer], "last": layer, "router_w": [N_r][d],
-              "router_b": [N_r]} with [out][in] matrices (numpy or torch) and fp32 gains.
+              "router_b": [N_r]} with [out][in] matrices (numpy or torch) and fp32 gains;
+              "first"/"last" are None (or absent) under cycle / sequence sharing.
     """
 
     LAYER_KEYS = (("wq", "wq"), ("wk", "wk"), ("wv", "wv"), ("wo", "wo"), ("w_gate", "wg"),
@@ -184,8 +232,10 @@ class Mor:
             return bw
 
         w = mor_weights()
-        w.first = block(weights["first"])
-        w.last = block(weights["last"])
+        if weights.get("first") is not None:        # absent under cycle / sequence sharing
+            w.first = block(weights["first"])
+        if weights.get("last") is not None:
+            w.last = block(weights["last"])
         shared = (mor_block_weights * max(1, len(weights["shared"])))()
         for i, layer in enumerate(weights["shared"]):
             shared[i] = block(layer)

@@ -120,17 +120,37 @@ namespace {
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
+// Sharing scheme helpers (mor_sharing). Under MIDDLE_* sharing the first and last layers are
+// unique and the N_r recursions share the L-2 layers between them; otherwise all L are shared.
+bool middle_sharing(const mor_config& c) {
+  return c.sharing == MOR_SHARE_MIDDLE_CYCLE || c.sharing == MOR_SHARE_MIDDLE_SEQUENCE;
+}
+int shared_per_rec(const mor_config& c) {
+  return (middle_sharing(c) ? c.n_layers - 2 : c.n_layers) / c.n_rec;
+}
+// Shared block (1..n_s) of position j (1..n_s) of recursion r (1..N_r): the cycle schemes reuse
+// block j at every recursion; the sequence schemes repeat each block on N_r consecutive layers.
+int block_of(const mor_config& c, int n_s, int r, int j) {
+  if (c.sharing == MOR_SHARE_MIDDLE_CYCLE || c.sharing == MOR_SHARE_CYCLE) return j;
+  const int u = (r - 1) * n_s + (j - 1);
+  return u / c.n_rec + 1;
+}
+
 mor_status validate(const mor_config* c) {
   if (!c) return fail(MOR_E_INVALID, "null config");
   if (c->dtype != MOR_F32 && c->dtype != MOR_BF16) return fail(MOR_E_INVALID, "dtype");
   if (c->routing < 0 || c->routing > 2) return fail(MOR_E_INVALID, "routing");
   if (c->kv_mode < 0 || c->kv_mode > 1) return fail(MOR_E_INVALID, "kv_mode");
   if (c->gate_mode < 0 || c->gate_mode > 1) return fail(MOR_E_INVALID, "gate_mode");
+  if (c->sharing < 0 || c->sharing > 3) return fail(MOR_E_INVALID, "sharing");
   if (c->d_model <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
-      c->d_ff <= 0 || c->n_layers < 3 || c->n_rec < 1 || c->n_rec > MOR_MAX_REC)
+      c->d_ff <= 0 || c->n_rec < 1 || c->n_rec > MOR_MAX_REC)
     return fail(MOR_E_INVALID, "non-positive dimension or n_rec outside 1..8");
-  if ((c->n_layers - 2) % c->n_rec) return fail(MOR_E_INVALID, "(n_layers - 2) % n_rec != 0");
-  const int n_s = (c->n_layers - 2) / c->n_rec;
+  const int span = middle_sharing(*c) ? c->n_layers - 2 : c->n_layers;
+  if (span < c->n_rec || span % c->n_rec)
+    return fail(MOR_E_INVALID, middle_sharing(*c) ? "n_layers - 2 must be a positive multiple of n_rec"
+                                                  : "n_layers must be a positive multiple of n_rec");
+  const int n_s = span / c->n_rec;
   if (n_s > MOR_MAX_SHARED) return fail(MOR_E_SHAPE, "more than 64 shared layers");
   if (c->d_model % 64 || c->d_ff % 64) return fail(MOR_E_SHAPE, "d_model and d_ff must be multiples of 64");
   if (c->dtype == MOR_BF16 && c->head_dim != 64) return fail(MOR_E_SHAPE, "bf16 needs head_dim 64");
@@ -152,6 +172,7 @@ mor_status validate(const mor_config* c) {
   if (c->max_slots < 0 || c->max_slots > 64) return fail(MOR_E_SHAPE, "max_slots must be 0..64");
   if (c->max_slots > 0) {
     if (c->routing != MOR_ROUTE_THRESHOLD) return fail(MOR_E_INVALID, "decode needs threshold routing");
+    if (c->sharing != MOR_SHARE_MIDDLE_CYCLE) return fail(MOR_E_INVALID, "decode needs middle-cycle sharing");
     const int P = c->kv_page_tokens;
     if (P != 16 && P != 32 && P != 64 && P != 128) return fail(MOR_E_SHAPE, "kv_page_tokens must be 16, 32, 64 or 128");
     if (c->kv_pages < 0 || c->max_requests < 1) return fail(MOR_E_INVALID, "kv_pages >= 0, max_requests >= 1");
@@ -165,7 +186,7 @@ mor_status validate(const mor_config* c) {
 // Walks the workspace; with base == nullptr only sizes it.
 size_t plan(const mor_config& c, mor_handle_s* h, char* base) {
   Cursor cur{base};
-  const int n_s = (c.n_layers - 2) / c.n_rec;
+  const int n_s = shared_per_rec(c);
   const size_t es = c.dtype == MOR_BF16 ? 2 : 4;
   const size_t d = c.d_model, dff = c.d_ff, hd = c.head_dim;
   const size_t nq = c.n_q_heads * hd, nkv = c.n_kv_heads * hd, nqkv = nq + 2 * nkv;
@@ -389,9 +410,13 @@ mor_status prefill_impl(mor_handle_s* h, const float* h_in, int B, int T, float*
     HIPCHK(launch_fill_f32(h->z + MT, R * MT, NAN, s));
 
   const RowSet all{meta_r[0], cnt_r(0), h->rows_all, (int)BT, T};
-  const KeySet keys_first{kv_k(h, 0), kv_vt(h, 0), act_r(0), cnt_r(0)};
-  mor_status st = run_layer<E>(h, h->blk[0], H, all, kv_k(h, 0), kv_vt(h, 0), keys_first, B, T, s);
-  if (st != MOR_OK) return st;
+  const bool middle = middle_sharing(c);
+  mor_status st = MOR_OK;
+  if (middle) {
+    const KeySet keys_first{kv_k(h, 0), kv_vt(h, 0), act_r(0), cnt_r(0)};
+    st = run_layer<E>(h, h->blk[0], H, all, kv_k(h, 0), kv_vt(h, 0), keys_first, B, T, s);
+    if (st != MOR_OK) return st;
+  }
   if (h_per_rec) HIPCHK(hipMemcpyAsync(h_per_rec, H, hbytes, hipMemcpyDeviceToDevice, s));
 
   const bool tc = c.routing == MOR_ROUTE_TOKEN_CHOICE;
@@ -416,14 +441,15 @@ mor_status prefill_impl(mor_handle_s* h, const float* h_in, int B, int T, float*
     const RowSet rs{meta_r[r], cnt_r(r), h->rows, m_up, per_seq};
     for (int j = 1; j <= n_s; ++j) {
       const int sid = 1 + (r - 1) * n_s + (j - 1);
+      const BlockPacked& wj = h->blk[block_of(c, n_s, r, j)];
       const bool share = c.kv_mode == MOR_KV_SHARE_FIRST && r >= 2;
       if (share) {
         const int s1 = 1 + (j - 1);
         const KeySet ks1{kv_k(h, s1), kv_vt(h, s1), act_r(1), cnt_r(1)};
-        st = run_layer<E>(h, h->blk[j], h->X, rs, nullptr, nullptr, ks1, B, T, s);
+        st = run_layer<E>(h, wj, h->X, rs, nullptr, nullptr, ks1, B, T, s);
       } else {
         const KeySet kr{kv_k(h, sid), kv_vt(h, sid), act_r(r), cnt_r(r)};
-        st = run_layer<E>(h, h->blk[j], h->X, rs, kv_k(h, sid), kv_vt(h, sid), kr, B, T, s);
+        st = run_layer<E>(h, wj, h->X, rs, kv_k(h, sid), kv_vt(h, sid), kr, B, T, s);
       }
       if (st != MOR_OK) return st;
     }
@@ -434,10 +460,12 @@ mor_status prefill_impl(mor_handle_s* h, const float* h_in, int B, int T, float*
     if (h_per_rec)
       HIPCHK(hipMemcpyAsync(h_per_rec + (size_t)r * BT * d, H, hbytes, hipMemcpyDeviceToDevice, s));
   }
-  const int last = 1 + R * n_s;
-  const KeySet keys_last{kv_k(h, last), kv_vt(h, last), act_r(0), cnt_r(0)};
-  st = run_layer<E>(h, h->blk[n_s + 1], H, all, kv_k(h, last), kv_vt(h, last), keys_last, B, T, s);
-  if (st != MOR_OK) return st;
+  if (middle) {
+    const int last = 1 + R * n_s;
+    const KeySet keys_last{kv_k(h, last), kv_vt(h, last), act_r(0), cnt_r(0)};
+    st = run_layer<E>(h, h->blk[n_s + 1], H, all, kv_k(h, last), kv_vt(h, last), keys_last, B, T, s);
+    if (st != MOR_OK) return st;
+  }
 
   for (int r = 1; r <= R; ++r) {
     if (sel_pos)
@@ -581,7 +609,8 @@ mor_status mor_init(const mor_config* cfg, const mor_weights* w, void* workspace
   if (st != MOR_OK) return st;
   if (!w || !workspace || !out) return fail(MOR_E_INVALID, "null weights, workspace or out");
   if (!w->router_w) return fail(MOR_E_INVALID, "null router_w");
-  const int n_s = (cfg->n_layers - 2) / cfg->n_rec;
+  const int n_s = shared_per_rec(*cfg);
+  const bool middle = middle_sharing(*cfg);
   if (!w->shared) return fail(MOR_E_INVALID, "null shared weights");
   const size_t need = plan(*cfg, nullptr, nullptr);
   if (workspace_bytes < need)
@@ -593,6 +622,7 @@ mor_status mor_init(const mor_config* cfg, const mor_weights* w, void* workspace
   plan(*cfg, h, base);
   auto cleanup = [&](mor_status e) { delete h; return e; };
   for (int i = 0; i < n_s + 2; ++i) {
+    if (!middle && (i == 0 || i == n_s + 1)) continue;    // no unique layers to pack
     const mor_block_weights& src = i == 0 ? w->first : i == n_s + 1 ? w->last : w->shared[i - 1];
     st = cfg->dtype == MOR_BF16 ? copy_block<bf16>(h, src, h->blk[i], s) : copy_block<float>(h, src, h->blk[i], s);
     if (st != MOR_OK) return cleanup(st);

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define MOR_ABI_VERSION 2
+#define MOR_ABI_VERSION 3
 #define MOR_MAX_REC 8
 #define MOR_MAX_SHARED 64
 
@@ -67,11 +67,26 @@ typedef enum { MOR_KV_RECURSION_WISE = 0, MOR_KV_SHARE_FIRST = 1 } mor_kv_mode;
 /* Gate of the recursion update: ROUTER merges H + g (F(H) - H) with g = sigmoid(z) (expert choice,
  * threshold) or the chosen-depth softmax weight (token choice); UNIT assigns H = F(H). */
 typedef enum { MOR_GATE_ROUTER = 0, MOR_GATE_UNIT = 1 } mor_gate_mode;
+/* Parameter sharing (MoR paper A.1; reading notes section 1): how the L unrolled layers map onto
+ * the pool of n_s shared blocks. The N_r routed recursions are consecutive spans of n_s layers.
+ *  MIDDLE_CYCLE:    unique first and last layers; n_s = (L-2)/N_r; position j of every recursion
+ *                   uses shared block j (the MoR default).
+ *  MIDDLE_SEQUENCE: unique first and last layers; interior layer u = 0..L-3 uses block u / N_r.
+ *  CYCLE:           no unique layers; n_s = L/N_r; position j of every recursion uses block j.
+ *  SEQUENCE:        no unique layers; layer u = 0..L-1 uses block u / N_r.
+ * Without unique layers recursion 1 routes the input H^0 and the output is H after recursion N_r.
+ * Depth-wise batched decode (max_slots > 0) needs MIDDLE_CYCLE: it runs one position j for every
+ * depth with the same block. Under SHARE_FIRST a recursion r >= 2 layer reads the recursion-1
+ * K/V of the same position j. */
+typedef enum {
+  MOR_SHARE_MIDDLE_CYCLE = 0, MOR_SHARE_MIDDLE_SEQUENCE = 1, MOR_SHARE_CYCLE = 2, MOR_SHARE_SEQUENCE = 3
+} mor_sharing;
 
 typedef struct {
   int32_t d_model, n_q_heads, n_kv_heads, head_dim, d_ff;
-  int32_t n_layers;              /* L, unrolled depth, first and last layer included            */
-  int32_t n_rec;                 /* N_r, 1..MOR_MAX_REC; (L - 2) % N_r == 0                      */
+  int32_t n_layers;              /* L, unrolled depth (unique first and last layer included)      */
+  int32_t n_rec;                 /* N_r, 1..MOR_MAX_REC; (L - 2) % N_r == 0 under MIDDLE_* sharing,
+                                    L % N_r == 0 otherwise                                       */
   int32_t cap_num[MOR_MAX_REC];  /* capacity of recursion r = cap_num[r-1] / cap_den, non-increasing, <= 1 */
   int32_t cap_den;
   int32_t routing;               /* mor_routing   */
@@ -88,6 +103,7 @@ typedef struct {
   int32_t kv_pages;              /* pages in the pool; 0 = enough for max_slots sequences of max_seq
                                     tokens that all run every recursion                             */
   int32_t max_requests;          /* requests one mor_decode_submit may queue                       */
+  int32_t sharing;               /* a mor_sharing value, 0 = MIDDLE_CYCLE                           */
 } mor_config;
 
 /* One Llama decoder layer. All device pointers. [out][in] matrices in the config dtype:
@@ -99,8 +115,8 @@ typedef struct {
 } mor_block_weights;
 
 typedef struct {
-  mor_block_weights first, last;
-  const mor_block_weights* shared;  /* host array of n_s = (L-2)/N_r entries (shared layer j = 1..n_s) */
+  mor_block_weights first, last;    /* unique layers (ignored under CYCLE and SEQUENCE sharing)     */
+  const mor_block_weights* shared;  /* host array of the n_s shared blocks (block j = 1..n_s)       */
   const float* router_w;            /* device fp32 [N_r][d]: row r-1 is theta_r (EC, threshold) or Theta_r (TC) */
   const float* router_b;            /* device fp32 [N_r] (threshold biases b_r), or NULL for zeros */
 } mor_weights;
@@ -132,7 +148,8 @@ mor_status mor_init(const mor_config* cfg, const mor_weights* w, void* workspace
  *   counts    int32 [N_r][B]     number of active tokens per recursion and sequence.
  *   logits    fp32  [N_r][B][T]  EC/threshold: z^r_t for t active at r-1 (NaN elsewhere);
  *                                TC: Theta_r . H^1_t for every t.
- *   h_per_rec fp32  [N_r+1][B][T][d] H after the first layer and after each recursion.
+ *   h_per_rec fp32  [N_r+1][B][T][d] H after the first layer (the input under CYCLE / SEQUENCE
+ *                                sharing) and after each recursion.
  * Router logits are computed in fp32 in one fixed order: lane l (0..63) accumulates
  * p = p + x[i]*w[i] over i = l, l+64, ... with the product and the sum rounded separately,
  * then p = p + p[l+o] for o = 32,16,...,1; bias, if any, is added last. Expert-choice selects
@@ -155,7 +172,8 @@ mor_status mor_route(mor_handle* h, const float* H, const int32_t* active_in,
                      int32_t* active_out, int32_t* counts_out, float* z_out, void* stream);
 
 /* Where the K/V cache of one layer stream lives after mor_prefill.
- * stream 0 = first layer, 1 + (r-1)*n_s + (j-1) = shared layer j at recursion r, 1 + N_r*n_s = last.
+ * stream 0 = first layer, 1 + (r-1)*n_s + (j-1) = position j of recursion r, 1 + N_r*n_s = last
+ * (streams 0 and 1 + N_r*n_s are not written under CYCLE / SEQUENCE sharing).
  * K is [B][kpad][Hkv][hd] (row = index of the token in that recursion's active list) and
  * V is stored transposed as [B][Hkv][hd][kpad]; kpad = max_seq rounded up to 64; dtype = config.
  * Under SHARE_FIRST the streams of recursions >= 2 are not written. */

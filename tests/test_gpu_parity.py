@@ -80,6 +80,44 @@ def test_small_f32_kv_share_free_running():
     _compare_prefill(workload.get_config("small_share_bf16", dtype="f32"))
 
 
+@pytest.mark.parametrize("scheme,L", [("middle_sequence", 8), ("cycle", 9), ("sequence", 9)])
+def test_small_f32_sharing_schemes_free_running(scheme, L):
+    """The other parameter-sharing schemes: same kernels, another layer-to-block schedule."""
+    _compare_prefill(workload.get_config("small_f32", sharing=scheme, n_layers=L))
+
+
+@pytest.mark.parametrize("scheme,L", [("middle_sequence", 8), ("cycle", 6), ("sequence", 9)])
+def test_small_bf16_sharing_schemes(scheme, L):
+    _compare_prefill(workload.get_config("small_bf16", sharing=scheme, n_layers=L))
+
+
+def test_small_bf16_sequence_sharing_with_kv_share():
+    """Recursive KV sharing under Sequence sharing: position j of recursion r >= 2 reads the
+    recursion-1 K/V of position j, computed there by another block."""
+    _compare_prefill(workload.get_config("small_share_bf16", sharing="sequence", n_layers=9))
+
+
+def test_small_f32_cycle_token_choice_free_running():
+    _compare_prefill(workload.get_config("small_tc_bf16", dtype="f32", sharing="cycle", n_layers=6))
+
+
+def test_test_time_recursion_scaling_bf16():
+    """One recursion more than trained, over the same shared pool: parity with the oracle on the
+    deeper configuration, and its first N_r recursions bitwise those of the trained depth."""
+    import adaptive_depth_recursive_amd as mor
+    cfg = workload.get_config("small_bf16")
+    W = workload.make_weights(cfg)
+    cfg2, W2 = mor.extend_recursions(cfg, W)
+    res2 = _compare_prefill(cfg2, weights=W2)
+    model, _ = build_gpu(cfg, W)
+    res = run_prefill(model, workload.make_inputs(cfg))
+    model.close()
+    for r in range(cfg.n_rec + 1):
+        assert np.array_equal(res["h_per_rec"][r], res2["h_per_rec"][r]), f"stage {r}"
+    for r in range(cfg.n_rec):
+        assert np.array_equal(res["sel_pos"][r], res2["sel_pos"][r]), f"set {r + 1}"
+
+
 def test_small_threshold_bf16():
     cfg = workload.get_config("small_thr_bf16")
     W = workload.make_weights(cfg)

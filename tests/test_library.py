@@ -31,7 +31,7 @@ def test_header_symbols_exported():
 
 def test_abi_version():
     mor = _lib()
-    assert mor.lib().mor_abi_version() == 2
+    assert mor.lib().mor_abi_version() == 3
 
 
 @pytest.mark.parametrize("name", sorted(workload.CONFIGS))
@@ -47,13 +47,25 @@ def test_workspace_bytes_for_every_config(name):
 
 @pytest.mark.parametrize("field,value", [
     ("d_model", 100), ("head_dim", 48), ("n_layers", 9), ("n_kv_heads", 7), ("cap_den", 0),
-    ("max_seq", 9000), ("n_rec", 9)])
+    ("max_seq", 9000), ("n_rec", 9), ("sharing", 4), ("sharing", -1)])
 def test_invalid_configs_rejected(field, value):
     mor = _lib()
     c = mor.make_config(workload.get_config("small_bf16"))
     setattr(c, field, value)
     assert mor.lib().mor_workspace_bytes(ctypes.byref(c)) == 0
     assert mor.lib().mor_last_error()
+
+
+@pytest.mark.parametrize("scheme,L,ok", [
+    ("middle_cycle", 8, True), ("middle_sequence", 8, True), ("cycle", 9, True), ("sequence", 9, True),
+    ("cycle", 8, False), ("sequence", 10, False), ("middle_sequence", 9, False), ("cycle", 3, True),
+    ("cycle", 2, False)])
+def test_sharing_scheme_layer_counts(scheme, L, ok):
+    """Middle schemes need L - 2 = N_r n_s, the others L = N_r n_s (n_s >= 1)."""
+    mor = _lib()
+    cfg = workload.get_config("small_bf16", sharing=scheme, n_layers=L)
+    n = mor.lib().mor_workspace_bytes(ctypes.byref(mor.make_config(cfg)))
+    assert (n > 0) == ok, mor.lib().mor_last_error()
 
 
 def test_increasing_capacities_rejected():
@@ -92,7 +104,7 @@ def test_null_handle_calls_rejected():
 
 @pytest.mark.parametrize("field,value", [
     ("max_slots", 65), ("kv_page_tokens", 48), ("routing", 0), ("max_requests", 0), ("kv_pages", -1),
-    ("d_model", 4160)])
+    ("d_model", 4160), ("sharing", 1), ("sharing", 2)])
 def test_invalid_decode_configs_rejected(field, value):
     mor = _lib()
     c = mor.make_config(workload.get_config("small_thr_bf16"), max_slots=5, kv_page_tokens=16,
