@@ -3,14 +3,23 @@
 // Same computation as the generic kernel in k_attn.hip (key s visible to query t iff
 // kpos[s] <= qpos[t]; S^T = K Q^T on MFMA, online softmax per query column, P^T fed to the PV
 // product as the B operand, V^T as the A operand), organised for throughput:
-//  - K and V^T tiles of 64 keys stream global -> LDS with global_load_lds_dwordx4 into two
-//    stages, so the next tile is in flight while this one is used;
+//  - K and V^T tiles of 64 keys, and their positions, stream global -> LDS with
+//    global_load_lds (no register round trip) into two stages, so the next tile is in flight
+//    while this one is used; the stages are separate LDS objects and the tile loop is unrolled
+//    by two, which lets the compiler see that the reads of one stage do not wait for the
+//    prefetch into the other;
 //  - the K tile rows are read in a permuted key order, chosen so that the 8 keys a lane holds
 //    for one PV step are 8 consecutive keys: the matching V^T operand is then one 16-byte LDS
 //    read, and the S^T accumulators need no shuffles to become the P^T operand;
-//  - K and V fragments are read once per tile and reused by all query heads of the KV head;
+//  - K and V fragments are read once per tile and reused by all query heads of the KV head, and
+//    the next head's S^T products are issued before this head's softmax (matrix cores and
+//    vector ALUs overlap within a wave);
 //  - the running maximum is only raised (and O rescaled) when it grows by more than 2^8, so the
-//    rescale is skipped on most tiles; probabilities are then bounded by 2^8, exact in fp32.
+//    rescale and its cross-lane reduction are skipped on most tiles; probabilities are then
+//    bounded by 2^8, exact in fp32;
+//  - workgroups are ordered so that each XCD owns whole (sequence, KV head) pairs, whose K/V then
+//    stay in that XCD's L2, with query blocks longest first; the key range of a block is found
+//    by a sampled wave-wide search while the first tile is already loading.
 #include <climits>
 
 #include "mor_internal.h"
@@ -60,9 +69,6 @@ __device__ __forceinline__ float max2f(float a, float b) {
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-constexpr bf16x2 kOnes2 = {(__bf16)1.f, (__bf16)1.f};
 
 __device__ __forceinline__ bf16x8 rd(const char* base, int row, int chunk, int sw) {
   return *reinterpret_cast<const bf16x8*>(base + row * kRow + ((chunk ^ sw) << 4));
@@ -125,8 +131,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
       __builtin_amdgcn_global_load_lds(kp + min(t0 + lane, nk - 1), (lds_void*)skp, 4, 0, 0);
   };
 
-  // Q is loaded once, pre-multiplied by scale * log2(e) and re-rounded to bf16, so that the
-  // S^T product comes out in base-2 exponent units.
+  // Q fragments of the G heads, loaded once (the bf16 values the projection stored).
   const float sl2 = a.scale_log2;
   const bf16* Qb = reinterpret_cast<const bf16*>(a.q);
   bf16x8 qf[G][2];
@@ -153,21 +158,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
   }
   const int kend = lo + __popcll(__ballot(lo + lane < hi && kp[lo + lane] <= maxpos));
 
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[hh][ks][e] = (bf16)((float)qf[hh][ks][e] * sl2);
-
-  // Per query (all four lanes that hold its column agree): reference maximum m in base-2 units,
-  // kept as the splat -m that seeds the S^T accumulators, so the product yields s * sl2 - m.
-  f32x4 nm4[G];
-  float lrun[G];
+  // Per query (all four lanes that hold its column agree): reference maximum m of the scores in
+  // base-2 units (score * scale * log2(e)), the running sum l of exp2(score * sl2 - m), and O.
+  float mrun[G], lrun[G];
   f32x4 o[G][4];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    nm4[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mrun[hh] = 0.f;
     lrun[hh] = 0.f;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) o[hh][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -223,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
     auto scores = [&](int hh, f32x4 (&s)[4]) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][0], qf[hh][0], nm4[hh], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][0], qf[hh][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
         s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][1], qf[hh][1], s[kb], 0, 0, 0);
@@ -238,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) s[kb] = sc[kb];
       if (hh + 1 < G) scores(hh + 1, sc);
-      // s[kb][e]: scaled score of key 32 (kb/2) + 8 g + 4 (kb & 1) + e of this tile, minus m
+      // s[kb][e]: raw score of key 32 (kb/2) + 8 g + 4 (kb & 1) + e of this tile
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -249,41 +246,39 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
                        max3f(s[1][2], s[1][3], s[2][0]));
       mx = max3f(mx, max3f(s[2][1], s[2][2], s[2][3]), max3f(s[3][0], s[3][1], s[3][2]));
       mx = max2f(mx, s[3][3]);
-      // m is raised (and O, l rescaled) only on the first tile or when a score exceeds it by
-      // more than 2^8; the vote is wave-wide, the new m is agreed within each query's lanes.
-      if (t == 0 || __any(mx > 8.f)) {
+      // m is set on the first tile and afterwards raised (with O and l rescaled) only when a
+      // score exceeds it by more than 2^8, so probabilities stay below 2^8 (exact in fp32); the
+      // vote is wave-wide, the new m is agreed within each query's four lanes.
+      if (t == 0 || __any(fmaf(mx, sl2, -mrun[hh]) > 8.f)) {
         mx = max2f(mx, __shfl_xor(mx, 16));
         mx = max2f(mx, __shfl_xor(mx, 32));
-        const float shift = t == 0 ? mx : fmaxf(mx, 0.f);
-        if (t > 0) {
-          const float alpha = __builtin_amdgcn_exp2f(-shift);
+        const float mloc = mx * sl2;
+        if (t == 0) {
+          mrun[hh] = mloc;
+        } else {
+          const float mnew = fmaxf(mrun[hh], mloc);
+          const float alpha = __builtin_amdgcn_exp2f(mrun[hh] - mnew);
           lrun[hh] *= alpha;
 #pragma unroll
           for (int hb = 0; hb < 4; ++hb) o[hh][hb] *= alpha;
+          mrun[hh] = mnew;
         }
-        const float nm = nm4[hh][0] - shift;
-        nm4[hh] = f32x4{nm, nm, nm, nm};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s[kb][e] -= shift;
       }
+      const float nm = -mrun[hh];
+      float pr[4][4];
       bf16x8 pf[2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pf[kb >> 1][4 * (kb & 1) + e] = (bf16)__builtin_amdgcn_exp2f(s[kb][e]);
-      // row sum of the bf16 probabilities the PV product uses: two-term dot products with
-      // (1, 1), in two chains
-      float l0 = lrun[hh], l1 = 0.f;
-#define MOR_PAIR_SUM(j)                                                                       \
-  l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[0], pf[0], 2 * j, 2 * j + 1), \
-                                       kOnes2, l0, false);                                    \
-  l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[1], pf[1], 2 * j, 2 * j + 1), \
-                                       kOnes2, l1, false);
-      MOR_PAIR_SUM(0) MOR_PAIR_SUM(1) MOR_PAIR_SUM(2) MOR_PAIR_SUM(3)
-#undef MOR_PAIR_SUM
-      lrun[hh] = l0 + l1;
+        for (int e = 0; e < 4; ++e) {
+          pr[kb][e] = __builtin_amdgcn_exp2f(fmaf(s[kb][e], sl2, nm));
+          pf[kb >> 1][4 * (kb & 1) + e] = (bf16)pr[kb][e];
+        }
+      // the normaliser sums the unrounded probabilities, as a tree (short dependency chains)
+      float ls[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) ls[kb] = (pr[kb][0] + pr[kb][1]) + (pr[kb][2] + pr[kb][3]);
+      lrun[hh] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
