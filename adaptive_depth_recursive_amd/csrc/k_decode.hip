@@ -459,19 +459,22 @@ hipError_t launch_dec_output(const DecArgs& a, int fold, hipStream_t s) {
 // Waves take 64-key tiles in turn. Scores: lane = key (its K row against the G query heads held
 // in LDS). Values: the tile's V rows are copied into LDS with 16-byte loads, then lane = head-dim
 // element accumulates over the tile's keys. The waves' partial results are merged in wave order.
-constexpr int DA_WAVES = 8;
+// Waves per (slot, KV head) workgroup: 16 where the LDS holds 16 waves' V tiles and
+// accumulators (bf16, up to 3 query heads per KV head), else 8; a context of n keys takes
+// ceil(n / (64 NW)) tiles per wave.
+template <typename T, int G> constexpr int dec_attn_waves() { return sizeof(T) == 2 && G <= 3 ? 16 : 8; }
 
-template <typename T, int HD, int G>
-__global__ __launch_bounds__(DA_WAVES * 64) void k_dec_attn(DecArgs a, int kind, int j) {
+template <typename T, int HD, int G, int NW = dec_attn_waves<T, G>()>
+__global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j) {
   constexpr int KT = 64;
   constexpr int CH = 16 / (int)sizeof(T);            // elements per 16-byte chunk
   constexpr int RCHUNKS = HD / CH;                   // chunks per K/V row
   __shared__ float sq[G][HD];
   __shared__ float skn[HD], svn[HD];
-  __shared__ float sp[DA_WAVES][G][KT];
-  __shared__ __attribute__((aligned(16))) T sv[DA_WAVES][KT * HD];
-  __shared__ float sm[DA_WAVES][G], sl[DA_WAVES][G];
-  __shared__ float sacc[DA_WAVES][G][HD];
+  __shared__ float sp[NW][G][KT];
+  __shared__ __attribute__((aligned(16))) T sv[NW][KT * HD];
+  __shared__ float sm[NW][G], sl[NW][G];
+  __shared__ float sacc[NW][G][HD];
 
   const int s = blockIdx.x, kvh = blockIdx.y;
   if (s >= a.S) return;
@@ -496,7 +499,7 @@ __global__ __launch_bounds__(DA_WAVES * 64) void k_dec_attn(DecArgs a, int kind,
   }
   const int half = HD / 2;
   const float* qkv = a.qkv + (size_t)s * a.nqkv;
-  for (int i = tid; i < (G + 2) * HD; i += DA_WAVES * 64) {
+  for (int i = tid; i < (G + 2) * HD; i += NW * 64) {
     const int hh = i / HD, c = i % HD;
     const int pc = c < half ? c + half : c - half;
     const float* base;
@@ -543,7 +546,7 @@ __global__ __launch_bounds__(DA_WAVES * 64) void k_dec_attn(DecArgs a, int kind,
   }
   const int* pt = a.ptab + ((size_t)s * a.LS + ls_r) * a.pps;
   T* svw = sv[wave];
-  for (int t0 = wave * KT; t0 < nkeys; t0 += DA_WAVES * KT) {
+  for (int t0 = wave * KT; t0 < nkeys; t0 += NW * KT) {
     const int nt = min(KT, nkeys - t0);
     // V rows of the tile -> LDS (16-byte chunks, consecutive lanes on consecutive chunks)
     for (int cidx = lane; cidx < nt * RCHUNKS; cidx += 64) {
@@ -612,9 +615,9 @@ __global__ __launch_bounds__(DA_WAVES * 64) void k_dec_attn(DecArgs a, int kind,
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       float M = -INFINITY;
-      for (int w = 0; w < DA_WAVES; ++w) M = fmaxf(M, sm[w][hh]);
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w][hh]);
       float L = 0.f, o = 0.f;
-      for (int w = 0; w < DA_WAVES; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float f = (sm[w][hh] == -INFINITY) ? 0.f : exp2f(sm[w][hh] - M);
         L += sl[w][hh] * f;
         o += sacc[w][hh][lane] * f;
@@ -626,12 +629,12 @@ __global__ __launch_bounds__(DA_WAVES * 64) void k_dec_attn(DecArgs a, int kind,
 
 template <typename T, int HD>
 static hipError_t dec_attn_g(const DecArgs& a, int kind, int j, hipStream_t s) {
-  dim3 grid(a.S, a.hkv), block(DA_WAVES * 64);
+  dim3 grid(a.S, a.hkv);
   switch (a.hq / a.hkv) {
-    case 1: hipLaunchKernelGGL((k_dec_attn<T, HD, 1>), grid, block, 0, s, a, kind, j); break;
-    case 2: hipLaunchKernelGGL((k_dec_attn<T, HD, 2>), grid, block, 0, s, a, kind, j); break;
-    case 3: hipLaunchKernelGGL((k_dec_attn<T, HD, 3>), grid, block, 0, s, a, kind, j); break;
-    case 4: hipLaunchKernelGGL((k_dec_attn<T, HD, 4>), grid, block, 0, s, a, kind, j); break;
+    case 1: hipLaunchKernelGGL((k_dec_attn<T, HD, 1>), grid, dim3(dec_attn_waves<T, 1>() * 64), 0, s, a, kind, j); break;
+    case 2: hipLaunchKernelGGL((k_dec_attn<T, HD, 2>), grid, dim3(dec_attn_waves<T, 2>() * 64), 0, s, a, kind, j); break;
+    case 3: hipLaunchKernelGGL((k_dec_attn<T, HD, 3>), grid, dim3(dec_attn_waves<T, 3>() * 64), 0, s, a, kind, j); break;
+    case 4: hipLaunchKernelGGL((k_dec_attn<T, HD, 4>), grid, dim3(dec_attn_waves<T, 4>() * 64), 0, s, a, kind, j); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
