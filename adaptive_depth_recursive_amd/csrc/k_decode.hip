@@ -221,6 +221,22 @@ hipError_t launch_dec_reset(const DecArgs& a, int n_req, hipStream_t s) {
 // gather_inputs (first layer), admitted slots first load their token's input hidden state into
 // X, and every other row of X is cleared; with fold > 0 the residual projection's partial sums
 // are first added into X (split order).
+// Split-K partial sums are added to a value in split order, exactly as a plain loop would. The
+// kMaxSplits loads are issued unconditionally and before the first add (splits past n re-read
+// split 0, a valid address, and are not added), so a fold costs one memory round trip instead of
+// one per split.
+constexpr int kMaxSplits = 8;
+template <typename V>
+__device__ __forceinline__ V fold_splits(V v, const V* p, size_t stride, int n) {
+  V pv[kMaxSplits];
+#pragma unroll
+  for (int q = 0; q < kMaxSplits; ++q) pv[q] = p[(q < n ? q : 0) * stride];
+#pragma unroll
+  for (int q = 0; q < kMaxSplits; ++q)
+    if (q < n) v = v + pv[q];
+  return v;
+}
+
 constexpr int ROW_THREADS = 256, ROW_CHUNKS = 4;   // rows up to 4096 elements
 
 __device__ __forceinline__ float block_sum_fixed(float v, float* red) {
@@ -254,11 +270,8 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_norm(DecArgs a, int gather,
       if (gather) {
         if (load_in) w = src[c];
       } else {
-        w = x[c];
-        for (int k = 0; k < fold; ++k) {
-          const float4 pv = reinterpret_cast<const float4*>(a.px + ((size_t)k * 64 + s) * d)[c];
-          w.x += pv.x; w.y += pv.y; w.z += pv.z; w.w += pv.w;
-        }
+        w = fold_splits(x[c], reinterpret_cast<const float4*>(a.px + (size_t)s * d) + c,
+                        (size_t)64 * d / 4, fold);
       }
       if (gather || fold) x[c] = w;
     }
@@ -283,7 +296,7 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_norm(DecArgs a, int gather,
 template <typename T>
 hipError_t launch_dec_norm(const DecArgs& a, bool gather_inputs, int fold, const float* g,
                            float eps, T* Xn, hipStream_t s) {
-  if (a.d > 4 * ROW_CHUNKS * ROW_THREADS) return hipErrorInvalidValue;
+  if (a.d > 4 * ROW_CHUNKS * ROW_THREADS || fold < 0 || fold > kMaxSplits) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_dec_norm<T>), dim3(a.S), dim3(ROW_THREADS), 0, s, a, gather_inputs ? 1 : 0,
                      fold, g, eps, Xn);
   return hipGetLastError();
@@ -313,26 +326,36 @@ constexpr int ROW_MAX = 4 * ROW_CHUNKS * ROW_THREADS;
 __global__ __launch_bounds__(ROW_THREADS) void k_dec_prep(DecArgs a, int fold) {
   __shared__ float prod[ROW_MAX];
   const int s = blockIdx.x, t = threadIdx.x;
-  if (!a.sl_part[s]) return;
-  const int d = a.d, r = a.sl_depth[s];
+  // the slot's state is read in one go (independent loads) before the participation test
+  const int part = a.sl_part[s], r = a.sl_depth[s], first = a.sl_first[s];
+  const int req = a.sl_req[s], pos = a.sl_pos[s];
+  if (!part) return;
+  const int d = a.d;
   float* __restrict__ x = a.X + (size_t)s * d;
   float* __restrict__ hs = a.Hs + (size_t)s * d;
   const float* __restrict__ w = a.router_w + (size_t)(r - 1) * d;
-  const int tok = a.req_off[a.sl_req[s]] + a.sl_pos[s];
-  const bool first = a.sl_first[s];
+  const int tok = a.req_off[req] + pos;
   float* __restrict__ dump = (first && a.h_dump) ? a.h_dump + ((size_t)tok * (a.R + 1)) * d : nullptr;
-  for (int c = t; c < d; c += ROW_THREADS) {
-    float h;
-    if (first) {
-      h = x[c];
-      for (int k = 0; k < fold; ++k) h += a.px[((size_t)k * 64 + s) * d + c];
-      hs[c] = h;                           // the folded first-layer output is the state...
-    } else {
-      h = hs[c];
+  // 4 elements per thread at a time: all their loads first, then the stores (a store to x or hs
+  // would otherwise order the next element's loads behind it)
+  for (int c0 = t; c0 < d; c0 += 4 * ROW_THREADS) {
+    float h[4], wv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = min(c0 + k * ROW_THREADS, d - 1);   // loads clamped in range, stores guarded
+      wv[k] = w[c];
+      h[k] = first ? fold_splits(x[c], a.px + (size_t)s * d + c, (size_t)64 * d, fold) : hs[c];
     }
-    x[c] = h;                              // ...and the shared block's input
-    if (dump) dump[c] = h;
-    prod[c] = mul_rn(h, w[c]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = c0 + k * ROW_THREADS;
+      if (c < d) {
+        if (first) hs[c] = h[k];           // the folded first-layer output is the state...
+        x[c] = h[k];                       // ...and the shared block's input
+        if (dump) dump[c] = h[k];
+        prod[c] = mul_rn(h[k], wv[k]);
+      }
+    }
   }
   __syncthreads();
   if (t >= WAVE) return;
@@ -345,6 +368,7 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_prep(DecArgs a, int fold) {
 }
 
 hipError_t launch_dec_prep(const DecArgs& a, int fold, hipStream_t s) {
+  if (fold < 0 || fold > kMaxSplits) return hipErrorInvalidValue;
   if (a.d > ROW_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_dec_prep, dim3(a.S), dim3(ROW_THREADS), 0, s, a, fold);
   return hipGetLastError();
@@ -356,23 +380,36 @@ hipError_t launch_dec_prep(const DecArgs& a, int fold, hipStream_t s) {
 __global__ __launch_bounds__(ROW_THREADS) void k_dec_update(DecArgs a, int fold) {
   __shared__ float prod[ROW_MAX];
   const int s = blockIdx.x, t = threadIdx.x;
-  if (!a.sl_part[s]) return;
-  const int d = a.d, r = a.sl_depth[s];
+  const int part = a.sl_part[s], r = a.sl_depth[s], req = a.sl_req[s], pos = a.sl_pos[s];
   const float g = a.gate[s];
+  if (!part) return;
+  const int d = a.d;
   float* __restrict__ x = a.X + (size_t)s * d;
   float* __restrict__ hs = a.Hs + (size_t)s * d;
-  const int tok = a.req_off[a.sl_req[s]] + a.sl_pos[s];
+  const int tok = a.req_off[req] + pos;
   const float* __restrict__ w = (r < a.R) ? a.router_w + (size_t)r * d : nullptr;
   float* __restrict__ dump = a.h_dump ? a.h_dump + ((size_t)tok * (a.R + 1) + r) * d : nullptr;
-  for (int c = t; c < d; c += ROW_THREADS) {
-    float xv = x[c];
-    for (int k = 0; k < fold; ++k) xv += a.px[((size_t)k * 64 + s) * d + c];
-    const float hv = hs[c];
-    const float hn = (g < 0.f) ? xv : hv + g * (xv - hv);
-    hs[c] = hn;
-    x[c] = hn;
-    if (dump) dump[c] = hn;
-    if (w) prod[c] = mul_rn(hn, w[c]);
+  // 4 elements per thread at a time: all their loads first, then the stores
+  for (int c0 = t; c0 < d; c0 += 4 * ROW_THREADS) {
+    float hn[4], wv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = min(c0 + k * ROW_THREADS, d - 1);   // loads clamped in range, stores guarded
+      const float xv = fold_splits(x[c], a.px + (size_t)s * d + c, (size_t)64 * d, fold);
+      const float hv = hs[c];
+      hn[k] = (g < 0.f) ? xv : hv + g * (xv - hv);
+      wv[k] = w ? w[c] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = c0 + k * ROW_THREADS;
+      if (c < d) {
+        hs[c] = hn[k];
+        x[c] = hn[k];
+        if (dump) dump[c] = hn[k];
+        if (w) prod[c] = mul_rn(hn[k], wv[k]);
+      }
+    }
   }
   __syncthreads();
   if (t >= WAVE) return;
@@ -397,6 +434,7 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_update(DecArgs a, int fold)
 }
 
 hipError_t launch_dec_update(const DecArgs& a, int fold, hipStream_t s) {
+  if (fold < 0 || fold > kMaxSplits) return hipErrorInvalidValue;
   if (a.d > ROW_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_dec_update, dim3(a.S), dim3(ROW_THREADS), 0, s, a, fold);
   return hipGetLastError();
@@ -431,12 +469,8 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_output(DecArgs a, int fold)
   const float4* x = reinterpret_cast<const float4*>(a.X + (size_t)s * d);
   float4* o = reinterpret_cast<float4*>(a.outputs + (size_t)tok * d);
   for (int c = t; c < d / 4; c += ROW_THREADS) {
-    float4 v = x[c];
-    for (int k = 0; k < fold; ++k) {
-      const float4 pv = reinterpret_cast<const float4*>(a.px + ((size_t)k * 64 + s) * d)[c];
-      v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
-    }
-    o[c] = v;
+    o[c] = fold_splits(x[c], reinterpret_cast<const float4*>(a.px + (size_t)s * d) + c,
+                       (size_t)64 * d / 4, fold);
   }
   if (t == 0) {
     a.sl_depth[s] = 0;                     // the exit flag is cleared by the next schedule
@@ -446,6 +480,7 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_output(DecArgs a, int fold)
 }
 
 hipError_t launch_dec_output(const DecArgs& a, int fold, hipStream_t s) {
+  if (fold < 0 || fold > kMaxSplits) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_dec_output, dim3(a.S), dim3(ROW_THREADS), 0, s, a, fold);
   return hipGetLastError();
 }
@@ -507,8 +542,9 @@ __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j
     else if (hh == G) base = qkv + a.nq + kvh * HD;
     else base = qkv + a.nq + a.nkv + kvh * HD;
     const size_t split = (size_t)64 * a.nqkv;     // partial sums of the K splits, added in order
-    float v = base[c], vp = base[pc];
-    for (int k = 1; k < a.kqkv; ++k) { v += base[k * split + c]; vp += base[k * split + pc]; }
+    const float v0 = fold_splits(base[c], base + split + c, split, a.kqkv - 1);
+    const float vp = fold_splits(base[pc], base + split + pc, split, a.kqkv - 1);
+    float v = v0;
     if (hh <= G) {
       const int f = c % half;
       const float cs = a.rope_cos[pos * half + f], sn = a.rope_sin[pos * half + f];
