@@ -769,12 +769,13 @@ hipError_t launch_dec_prefix(const DecArgs& a, const PrefixSrc& p, hipStream_t s
 // out^T = W . A^T for the 64 rows of A (the slots), weights on the MFMA A side. A workgroup owns
 // RG groups of 16 weight rows and one contiguous range of 128-byte K slices (K is split over
 // grid.y so that enough CUs stream the weights); its 4 waves take the range's slices in turn,
-// loading the fragments of SK_BATCH of their slices before multiplying them (several loads per
+// loading the fragments of SK_BATCH of their slices before multiplying them (SK_BATCH is the
+// number of slices a wave has, up to 4, so one round of loads usually covers them; several loads per
 // lane in flight), and add their partial sums in wave order in LDS (deterministic). Wave w then
 // finishes slot rows 16w..16w+15: each lane holds 4 consecutive output columns of one row.
-constexpr int SK_WAVES = 4, SK_BATCH = 3;
+constexpr int SK_WAVES = 4;
 
-template <typename T, int RG, int EPI>
+template <typename T, int RG, int EPI, int SK_BATCH>
 __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny(const T* __restrict__ A,
                                                           const T* __restrict__ W, int N, int K,
                                                           int M, SkinnyEpi ep) {
@@ -873,11 +874,23 @@ template <typename T>
 hipError_t launch_skinny(int epi, const T* A, const T* W, int N, int K, int M, int ksplit,
                          const SkinnyEpi& ep, hipStream_t s) {
   if (K % 64 || N % 32 || M > 64 || ksplit < 1 || ksplit > 8) return hipErrorInvalidValue;
+  // slices each wave handles: the batch covers them in one round of loads where registers allow
+  const int uk = 128 / (int)sizeof(T), per_split = (K / uk + ksplit - 1) / ksplit;
+  const int per_wave = (per_split + SK_WAVES - 1) / SK_WAVES;
+  const dim3 blk(SK_WAVES * 64);
   if (epi == SK_PARTIAL) {
-    hipLaunchKernelGGL((k_skinny<T, 1, SK_PARTIAL>), dim3(N / 16, ksplit), dim3(SK_WAVES * 64), 0, s, A, W, N, K, M, ep);
+    const dim3 grid(N / 16, ksplit);
+    if (per_wave <= 1) hipLaunchKernelGGL((k_skinny<T, 1, SK_PARTIAL, 1>), grid, blk, 0, s, A, W, N, K, M, ep);
+    else if (per_wave == 2) hipLaunchKernelGGL((k_skinny<T, 1, SK_PARTIAL, 2>), grid, blk, 0, s, A, W, N, K, M, ep);
+    else if (per_wave == 3) hipLaunchKernelGGL((k_skinny<T, 1, SK_PARTIAL, 3>), grid, blk, 0, s, A, W, N, K, M, ep);
+    else hipLaunchKernelGGL((k_skinny<T, 1, SK_PARTIAL, 4>), grid, blk, 0, s, A, W, N, K, M, ep);
   } else {
     if (ksplit != 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_skinny<T, 2, SK_SWIGLU>), dim3(N / 32, 1), dim3(SK_WAVES * 64), 0, s, A, W, N, K, M, ep);
+    const dim3 grid(N / 32, 1);
+    if (per_wave <= 1) hipLaunchKernelGGL((k_skinny<T, 2, SK_SWIGLU, 1>), grid, blk, 0, s, A, W, N, K, M, ep);
+    else if (per_wave == 2) hipLaunchKernelGGL((k_skinny<T, 2, SK_SWIGLU, 2>), grid, blk, 0, s, A, W, N, K, M, ep);
+    else if (per_wave == 3) hipLaunchKernelGGL((k_skinny<T, 2, SK_SWIGLU, 3>), grid, blk, 0, s, A, W, N, K, M, ep);
+    else hipLaunchKernelGGL((k_skinny<T, 2, SK_SWIGLU, 4>), grid, blk, 0, s, A, W, N, K, M, ep);
   }
   return hipGetLastError();
 }
