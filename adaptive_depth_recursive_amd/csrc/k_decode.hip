@@ -248,6 +248,45 @@ __device__ __forceinline__ float block_sum_fixed(float v, float* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
+__device__ __forceinline__ float sq4(float4 v) { return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w; }
+
+// Last step of an RMSNorm of a row held as float4 chunks (thread t holds chunks t, t + 256, ...)
+// with ss this thread's sum of squares: the workgroup sum, then out = v / rms * gain. Every
+// kernel that normalises a slot row ends with this, so the sum is grouped the same way in each.
+template <typename T>
+__device__ __forceinline__ void row_norm_store(const float4* v, const float4* gg, float ss, int nc,
+                                               int d, float eps, float* red, T* out) {
+  ss = block_sum_fixed(ss, red);
+  const float rinv = 1.f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int u = 0; u < ROW_CHUNKS; ++u) {
+    const int c = threadIdx.x + u * ROW_THREADS;
+    if (c < nc)
+      Vec4<T>::store(out + 4 * c, v[u].x * rinv * gg[u].x, v[u].y * rinv * gg[u].y,
+                     v[u].z * rinv * gg[u].z, v[u].w * rinv * gg[u].w);
+  }
+}
+
+// RMSNorm of a slot row of X as it stands (rows of slots that a fused kernel does not update).
+template <typename T>
+__device__ __forceinline__ void norm_row_as_is(const float4* x, const float* gain, int nc, int d,
+                                               float eps, float* red, T* out) {
+  const float4* g4 = reinterpret_cast<const float4*>(gain);
+  float4 v[ROW_CHUNKS], gg[ROW_CHUNKS];
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < ROW_CHUNKS; ++u) {
+    const int c = threadIdx.x + u * ROW_THREADS;
+    v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < nc) {
+      gg[u] = g4[c];
+      v[u] = x[c];
+    }
+    ss += sq4(v[u]);
+  }
+  row_norm_store<T>(v, gg, ss, nc, d, eps, red, out);
+}
+
 template <typename T>
 __global__ __launch_bounds__(ROW_THREADS) void k_dec_norm(DecArgs a, int gather, int fold,
                                                           const float* __restrict__ g, float eps,
@@ -260,13 +299,16 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_norm(DecArgs a, int gather,
   const float4* src = load_in ? reinterpret_cast<const float4*>(
                                     a.inputs + (size_t)(a.req_off[a.sl_req[s]] + a.sl_pos[s]) * d)
                               : nullptr;
-  float4 v[ROW_CHUNKS];
+  // the gains are loaded with the row, so the reduction is the only wait after the loads
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  float4 v[ROW_CHUNKS], gg[ROW_CHUNKS];
   float ss = 0.f;
 #pragma unroll
   for (int u = 0; u < ROW_CHUNKS; ++u) {
     const int c = t + u * ROW_THREADS;
     float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
     if (c < nc) {
+      gg[u] = g4[c];
       if (gather) {
         if (load_in) w = src[c];
       } else {
@@ -276,21 +318,9 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_norm(DecArgs a, int gather,
       if (gather || fold) x[c] = w;
     }
     v[u] = w;
-    ss += w.x * w.x + w.y * w.y + w.z * w.z + w.w * w.w;
+    ss += sq4(w);
   }
-  ss = block_sum_fixed(ss, red);
-  const float rinv = 1.f / sqrtf(ss / (float)d + eps);
-  const float4* g4 = reinterpret_cast<const float4*>(g);
-  T* out = Xn + (size_t)s * d;
-#pragma unroll
-  for (int u = 0; u < ROW_CHUNKS; ++u) {
-    const int c = t + u * ROW_THREADS;
-    if (c < nc) {
-      const float4 gg = g4[c];
-      Vec4<T>::store(out + 4 * c, v[u].x * rinv * gg.x, v[u].y * rinv * gg.y, v[u].z * rinv * gg.z,
-                     v[u].w * rinv * gg.w);
-    }
-  }
+  row_norm_store<T>(v, gg, ss, nc, d, eps, red, Xn + (size_t)s * d);
 }
 
 template <typename T>
@@ -322,42 +352,60 @@ constexpr int ROW_MAX = 4 * ROW_CHUNKS * ROW_THREADS;
 // Start of the recursion of every occupied slot: a newly admitted token's state is the first
 // layer's output (plus its down projection's partial sums), a continuing token's state is
 // carried in Hs; the shared block works on X. The gate of the recursion is
-// sigmoid(theta_r . H + b_r).
-__global__ __launch_bounds__(ROW_THREADS) void k_dec_prep(DecArgs a, int fold) {
+// sigmoid(theta_r . H + b_r). The first shared layer's RMSNorm of every slot row (gain, Xn) is
+// done here too, saving its launch.
+template <typename T>
+__global__ __launch_bounds__(ROW_THREADS) void k_dec_prep(DecArgs a, int fold, const float* __restrict__ gain,
+                                                          float eps, T* __restrict__ Xn) {
   __shared__ float prod[ROW_MAX];
+  __shared__ float red[4];
   const int s = blockIdx.x, t = threadIdx.x;
   // the slot's state is read in one go (independent loads) before the participation test
   const int part = a.sl_part[s], r = a.sl_depth[s], first = a.sl_first[s];
   const int req = a.sl_req[s], pos = a.sl_pos[s];
-  if (!part) return;
-  const int d = a.d;
-  float* __restrict__ x = a.X + (size_t)s * d;
-  float* __restrict__ hs = a.Hs + (size_t)s * d;
-  const float* __restrict__ w = a.router_w + (size_t)(r - 1) * d;
+  const int d = a.d, nc = d / 4;
+  float4* __restrict__ x = reinterpret_cast<float4*>(a.X + (size_t)s * d);
+  T* out = Xn + (size_t)s * d;
+  if (!part) {
+    norm_row_as_is<T>(x, gain, nc, d, eps, red, out);
+    return;
+  }
+  float4* __restrict__ hs = reinterpret_cast<float4*>(a.Hs + (size_t)s * d);
+  const float4* __restrict__ w = reinterpret_cast<const float4*>(a.router_w + (size_t)(r - 1) * d);
+  const float4* __restrict__ px = reinterpret_cast<const float4*>(a.px + (size_t)s * d);
+  const float4* g4 = reinterpret_cast<const float4*>(gain);
   const int tok = a.req_off[req] + pos;
-  float* __restrict__ dump = (first && a.h_dump) ? a.h_dump + ((size_t)tok * (a.R + 1)) * d : nullptr;
-  // 4 elements per thread at a time: all their loads first, then the stores (a store to x or hs
-  // would otherwise order the next element's loads behind it)
-  for (int c0 = t; c0 < d; c0 += 4 * ROW_THREADS) {
-    float h[4], wv[4];
+  float4* __restrict__ dump = (first && a.h_dump)
+                                  ? reinterpret_cast<float4*>(a.h_dump + ((size_t)tok * (a.R + 1)) * d)
+                                  : nullptr;
+  // all loads first, then the stores (a store to x or hs would otherwise order later loads behind it)
+  float4 h[ROW_CHUNKS], wv[ROW_CHUNKS], gg[ROW_CHUNKS];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int c = min(c0 + k * ROW_THREADS, d - 1);   // loads clamped in range, stores guarded
-      wv[k] = w[c];
-      h[k] = first ? fold_splits(x[c], a.px + (size_t)s * d + c, (size_t)64 * d, fold) : hs[c];
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int c = c0 + k * ROW_THREADS;
-      if (c < d) {
-        if (first) hs[c] = h[k];           // the folded first-layer output is the state...
-        x[c] = h[k];                       // ...and the shared block's input
-        if (dump) dump[c] = h[k];
-        prod[c] = mul_rn(h[k], wv[k]);
-      }
+  for (int u = 0; u < ROW_CHUNKS; ++u) {
+    const int c = t + u * ROW_THREADS;
+    h[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < nc) {
+      wv[u] = w[c];
+      gg[u] = g4[c];
+      h[u] = first ? fold_splits(x[c], px + c, (size_t)64 * d / 4, fold) : hs[c];
     }
   }
-  __syncthreads();
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < ROW_CHUNKS; ++u) {
+    const int c = t + u * ROW_THREADS;
+    if (c < nc) {
+      if (first) hs[c] = h[u];             // the folded first-layer output is the state...
+      x[c] = h[u];                         // ...and the shared block's input
+      if (dump) dump[c] = h[u];
+      prod[4 * c + 0] = mul_rn(h[u].x, wv[u].x);
+      prod[4 * c + 1] = mul_rn(h[u].y, wv[u].y);
+      prod[4 * c + 2] = mul_rn(h[u].z, wv[u].z);
+      prod[4 * c + 3] = mul_rn(h[u].w, wv[u].w);
+    }
+    ss += sq4(h[u]);
+  }
+  row_norm_store<T>(h, gg, ss, nc, d, eps, red, out);   // its barriers also publish prod
   if (t >= WAVE) return;
   const float z = row_logit_fixed(prod, d, a.router_b[r - 1]);
   if (t == 0) {
@@ -367,51 +415,80 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_prep(DecArgs a, int fold) {
   }
 }
 
-hipError_t launch_dec_prep(const DecArgs& a, int fold, hipStream_t s) {
+template <typename T>
+hipError_t launch_dec_prep(const DecArgs& a, int fold, const float* gain, float eps, T* Xn, hipStream_t s) {
   if (fold < 0 || fold > kMaxSplits) return hipErrorInvalidValue;
   if (a.d > ROW_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_dec_prep, dim3(a.S), dim3(ROW_THREADS), 0, s, a, fold);
+  hipLaunchKernelGGL((k_dec_prep<T>), dim3(a.S), dim3(ROW_THREADS), 0, s, a, fold, gain, eps, Xn);
   return hipGetLastError();
+}
+template hipError_t launch_dec_prep<float>(const DecArgs&, int, const float*, float, float*, hipStream_t);
+template hipError_t launch_dec_prep<bf16>(const DecArgs&, int, const float*, float, bf16*, hipStream_t);
+
+__device__ __forceinline__ float gate_mix(float g, float xv, float hv) {
+  return (g < 0.f) ? xv : hv + g * (xv - hv);
 }
 
 // End of the recursion: F(H) = X + the last shared layer's down-projection partial sums;
 // H <- H + g (F(H) - H) (or F(H) under unit gating), then the exit test on the next router
-// logit: the token continues iff r < N_r and theta_{r+1} . H + b_{r+1} > 0.
-__global__ __launch_bounds__(ROW_THREADS) void k_dec_update(DecArgs a, int fold) {
+// logit: the token continues iff r < N_r and theta_{r+1} . H + b_{r+1} > 0. The last layer's
+// RMSNorm of every slot row (gain, Xn) is done here too, saving its launch.
+template <typename T>
+__global__ __launch_bounds__(ROW_THREADS) void k_dec_update(DecArgs a, int fold, const float* __restrict__ gain,
+                                                            float eps, T* __restrict__ Xn) {
   __shared__ float prod[ROW_MAX];
+  __shared__ float red[4];
   const int s = blockIdx.x, t = threadIdx.x;
   const int part = a.sl_part[s], r = a.sl_depth[s], req = a.sl_req[s], pos = a.sl_pos[s];
   const float g = a.gate[s];
-  if (!part) return;
-  const int d = a.d;
-  float* __restrict__ x = a.X + (size_t)s * d;
-  float* __restrict__ hs = a.Hs + (size_t)s * d;
+  const int d = a.d, nc = d / 4;
+  float4* __restrict__ x = reinterpret_cast<float4*>(a.X + (size_t)s * d);
+  T* out = Xn + (size_t)s * d;
+  if (!part) {
+    norm_row_as_is<T>(x, gain, nc, d, eps, red, out);
+    return;
+  }
+  float4* __restrict__ hs = reinterpret_cast<float4*>(a.Hs + (size_t)s * d);
+  const float4* __restrict__ px = reinterpret_cast<const float4*>(a.px + (size_t)s * d);
+  const float4* g4 = reinterpret_cast<const float4*>(gain);
   const int tok = a.req_off[req] + pos;
-  const float* __restrict__ w = (r < a.R) ? a.router_w + (size_t)r * d : nullptr;
-  float* __restrict__ dump = a.h_dump ? a.h_dump + ((size_t)tok * (a.R + 1) + r) * d : nullptr;
-  // 4 elements per thread at a time: all their loads first, then the stores
-  for (int c0 = t; c0 < d; c0 += 4 * ROW_THREADS) {
-    float hn[4], wv[4];
+  const float4* __restrict__ w =
+      (r < a.R) ? reinterpret_cast<const float4*>(a.router_w + (size_t)r * d) : nullptr;
+  float4* __restrict__ dump =
+      a.h_dump ? reinterpret_cast<float4*>(a.h_dump + ((size_t)tok * (a.R + 1) + r) * d) : nullptr;
+  // all loads first, then the stores
+  float4 hn[ROW_CHUNKS], wv[ROW_CHUNKS], gg[ROW_CHUNKS];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int c = min(c0 + k * ROW_THREADS, d - 1);   // loads clamped in range, stores guarded
-      const float xv = fold_splits(x[c], a.px + (size_t)s * d + c, (size_t)64 * d, fold);
-      const float hv = hs[c];
-      hn[k] = (g < 0.f) ? xv : hv + g * (xv - hv);
-      wv[k] = w ? w[c] : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int c = c0 + k * ROW_THREADS;
-      if (c < d) {
-        hs[c] = hn[k];
-        x[c] = hn[k];
-        if (dump) dump[c] = hn[k];
-        if (w) prod[c] = mul_rn(hn[k], wv[k]);
-      }
+  for (int u = 0; u < ROW_CHUNKS; ++u) {
+    const int c = t + u * ROW_THREADS;
+    hn[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < nc) {
+      const float4 xv = fold_splits(x[c], px + c, (size_t)64 * d / 4, fold);
+      const float4 hv = hs[c];
+      gg[u] = g4[c];
+      wv[u] = w ? w[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      hn[u] = make_float4(gate_mix(g, xv.x, hv.x), gate_mix(g, xv.y, hv.y), gate_mix(g, xv.z, hv.z),
+                          gate_mix(g, xv.w, hv.w));
     }
   }
-  __syncthreads();
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < ROW_CHUNKS; ++u) {
+    const int c = t + u * ROW_THREADS;
+    if (c < nc) {
+      hs[c] = hn[u];
+      x[c] = hn[u];
+      if (dump) dump[c] = hn[u];
+      if (w) {
+        prod[4 * c + 0] = mul_rn(hn[u].x, wv[u].x);
+        prod[4 * c + 1] = mul_rn(hn[u].y, wv[u].y);
+        prod[4 * c + 2] = mul_rn(hn[u].z, wv[u].z);
+        prod[4 * c + 3] = mul_rn(hn[u].w, wv[u].w);
+      }
+    }
+    ss += sq4(hn[u]);
+  }
+  row_norm_store<T>(hn, gg, ss, nc, d, eps, red, out);  // its barriers also publish prod
   if (t >= WAVE) return;
   bool leave = true;
   if (w) {
@@ -433,12 +510,15 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_update(DecArgs a, int fold)
   }
 }
 
-hipError_t launch_dec_update(const DecArgs& a, int fold, hipStream_t s) {
+template <typename T>
+hipError_t launch_dec_update(const DecArgs& a, int fold, const float* gain, float eps, T* Xn, hipStream_t s) {
   if (fold < 0 || fold > kMaxSplits) return hipErrorInvalidValue;
   if (a.d > ROW_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_dec_update, dim3(a.S), dim3(ROW_THREADS), 0, s, a, fold);
+  hipLaunchKernelGGL((k_dec_update<T>), dim3(a.S), dim3(ROW_THREADS), 0, s, a, fold, gain, eps, Xn);
   return hipGetLastError();
 }
+template hipError_t launch_dec_update<float>(const DecArgs&, int, const float*, float, float*, hipStream_t);
+template hipError_t launch_dec_update<bf16>(const DecArgs&, int, const float*, float, bf16*, hipStream_t);
 
 // Tokens that ran the last layer: output = X + the last layer's down-projection partial sums;
 // mark the token finished. Workgroup 0 also counts the last layer's algorithmic bytes.

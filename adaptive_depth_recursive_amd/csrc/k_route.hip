@@ -172,16 +172,34 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(int mode, int T, const f
         for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0;
         __syncthreads();
         const unsigned prefix = s_prefix;
+        const int rem = s_remaining;
         for (int i = tid; i < n; i += SEL_THREADS) {
           const unsigned key = skey[i];
           if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
         }
         __syncthreads();
-        if (tid == 0) {
-          int rem = s_remaining, dgt = 0;
-          while (hist[dgt] < rem) { rem -= hist[dgt]; ++dgt; }
-          s_remaining = rem;
-          s_prefix = prefix | ((unsigned)dgt << shift);
+        // the digit is the first bin whose inclusive count reaches rem: a scan of the 256 bins
+        // by waves 0-3 (shuffles within a wave, then the wave totals)
+        const int lane = tid & 63, wave = tid >> 6;
+        int hv = 0, incl = 0;
+        if (tid < 256) {
+          hv = hist[tid];
+          incl = hv;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+          }
+          if (lane == 63) swave[wave] = incl;
+        }
+        __syncthreads();
+        if (tid < 256) {
+          for (int w = 0; w < wave; ++w) incl += swave[w];
+          const int excl = incl - hv;
+          if (excl < rem && incl >= rem) {
+            s_remaining = rem - excl;
+            s_prefix = prefix | ((unsigned)tid << shift);
+          }
         }
         pmask |= 255u << shift;
         __syncthreads();

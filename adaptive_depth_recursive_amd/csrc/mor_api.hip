@@ -49,6 +49,23 @@ struct BlockPacked {
 
 constexpr size_t kAlign = 256;
 
+// K splits of the decode projections: enough workgroups to spread the weight streaming over the
+// CUs (a projection has only N/16 column groups of 64 slot rows). Their consumers fold at most
+// 8 partial sums besides the one they start from.
+#ifndef MOR_DEC_SPLIT_QKV
+#define MOR_DEC_SPLIT_QKV 4
+#endif
+#ifndef MOR_DEC_SPLIT_O
+#define MOR_DEC_SPLIT_O 4
+#endif
+#ifndef MOR_DEC_SPLIT_DOWN
+#define MOR_DEC_SPLIT_DOWN 4
+#endif
+constexpr int kSplitQKV = MOR_DEC_SPLIT_QKV, kSplitO = MOR_DEC_SPLIT_O, kSplitDown = MOR_DEC_SPLIT_DOWN;
+constexpr int kSplitPx = kSplitO > kSplitDown ? kSplitO : kSplitDown;
+static_assert(kSplitQKV >= 1 && kSplitQKV <= 8, "QKV split out of range");
+static_assert(kSplitO >= 1 && kSplitO <= 8 && kSplitDown >= 1 && kSplitDown <= 8, "split out of range");
+
 struct Cursor {
   char* base;
   size_t off = 0;
@@ -100,7 +117,7 @@ struct mor_handle_s {
   int* dreq_off = nullptr;       // [max_requests]
   void* dXn = nullptr;           // [64][d]
   float* dQkv = nullptr;         // [kSplitQKV][64][nqkv] partial sums
-  float* dPx = nullptr;          // [8][64][d] partial sums of the O / down projections
+  float* dPx = nullptr;          // [kSplitPx][64][d] partial sums of the O / down projections
   void* dO = nullptr;            // [64][nq]
   void* dHf = nullptr;           // [64][d_ff]
   bool submitted = false;
@@ -254,8 +271,8 @@ size_t plan(const mor_config& c, mor_handle_s* h, char* base) {
     da.Hs = cur.take<float>(64 * d * 4);
     da.gate = cur.take<float>(64 * 4);
     dXn = cur.take<void>(64 * d * es);
-    dQkv = cur.take<float>(4 * 64 * nqkv * 4);
-    dPx = cur.take<float>(8 * 64 * d * 4);
+    dQkv = cur.take<float>((size_t)kSplitQKV * 64 * nqkv * 4);
+    dPx = cur.take<float>((size_t)kSplitPx * 64 * d * 4);
     dO = cur.take<void>(64 * nq * es);
     dHf = cur.take<void>(64 * dff * es);
     da.pool = cur.take<void>((size_t)kv_pages * page_bytes);
@@ -286,7 +303,7 @@ size_t plan(const mor_config& c, mor_handle_s* h, char* base) {
       da.req_len = dreq_len; da.req_off = dreq_off;
       da.router_w = router_w; da.router_b = router_b;
       da.rope_cos = rope_cos; da.rope_sin = rope_sin;
-      da.qkv = dQkv; da.kqkv = 4; da.px = dPx; da.o = dO;
+      da.qkv = dQkv; da.kqkv = kSplitQKV; da.px = dPx; da.o = dO;
       da.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
       da.es = (int)es;
       da.layer_weight_bytes = (long long)((nqkv * d + d * nq + 2 * dff * d + d * dff) * es);
@@ -487,20 +504,19 @@ mor_status prefill_impl(mor_handle_s* h, const float* h_in, int B, int T, float*
 }
 
 // ------------------------------------------------------------------ decode iteration
-// K splits of the decode projections: enough workgroups to spread the weight streaming over the
-// CUs (a projection has only N/16 column groups of 64 slot rows).
-constexpr int kSplitQKV = 4, kSplitO = 4, kSplitDown = 8;
 
 // fold_in: residual partial sums of the previous layer still to be added into X (0 if X is
-// already complete). Returns through fold_out the partial sums this layer leaves (its down
-// projection's), which the next consumer of X adds.
+// already complete); fold_in < 0: the kernel before this layer already wrote its normalised
+// input Xn. The layer leaves its down projection's kSplitDown partial sums, which the next
+// consumer of X adds.
 template <typename E>
 mor_status dec_layer(mor_handle_s* h, const BlockPacked& w, int kind, int j, int fold_in, hipStream_t s) {
   const mor_config& c = h->cfg;
   const DecArgs& a = h->dec;
   const int d = c.d_model, dff = c.d_ff, S = a.S;
   E* Xn = reinterpret_cast<E*>(h->dXn);
-  HIPCHK(launch_dec_norm<E>(a, kind == DL_FIRST, kind == DL_FIRST ? 0 : fold_in, w.g_attn, c.rms_eps, Xn, s));
+  if (fold_in >= 0)
+    HIPCHK(launch_dec_norm<E>(a, kind == DL_FIRST, kind == DL_FIRST ? 0 : fold_in, w.g_attn, c.rms_eps, Xn, s));
   SkinnyEpi eq{};
   eq.out = h->dQkv; eq.ldo = h->nqkv;
   HIPCHK(launch_skinny<E>(SK_PARTIAL, Xn, reinterpret_cast<const E*>(w.wqkv), h->nqkv, d, S, kSplitQKV, eq, s));
@@ -522,13 +538,17 @@ mor_status dec_iteration(mor_handle_s* h, hipStream_t s) {
   HIPCHK(launch_dec_schedule(h->dec, s));
   mor_status st = dec_layer<E>(h, h->blk[0], DL_FIRST, 0, 0, s);
   if (st != MOR_OK) return st;
-  HIPCHK(launch_dec_prep(h->dec, kSplitDown, s));      // X of new tokens += first layer's down
+  E* Xn = reinterpret_cast<E*>(h->dXn);
+  const float eps = h->cfg.rms_eps;
+  // X of new tokens += first layer's down; then the first shared layer's input norm
+  HIPCHK(launch_dec_prep<E>(h->dec, kSplitDown, h->blk[1].g_attn, eps, Xn, s));
   for (int j = 1; j <= n_s; ++j) {
-    st = dec_layer<E>(h, h->blk[j], DL_SHARED, j, j == 1 ? 0 : kSplitDown, s);
+    st = dec_layer<E>(h, h->blk[j], DL_SHARED, j, j == 1 ? -1 : kSplitDown, s);
     if (st != MOR_OK) return st;
   }
-  HIPCHK(launch_dec_update(h->dec, kSplitDown, s));    // F(H) = X + last shared layer's down
-  st = dec_layer<E>(h, h->blk[n_s + 1], DL_LAST, 0, 0, s);
+  // F(H) = X + last shared layer's down, the gated update and exit test; then the last layer's norm
+  HIPCHK(launch_dec_update<E>(h->dec, kSplitDown, h->blk[n_s + 1].g_attn, eps, Xn, s));
+  st = dec_layer<E>(h, h->blk[n_s + 1], DL_LAST, 0, -1, s);
   if (st != MOR_OK) return st;
   HIPCHK(launch_dec_output(h->dec, kSplitDown, s));    // output = X + last layer's down
   return MOR_OK;

@@ -141,8 +141,12 @@ hipError_t launch_dec_schedule(const DecArgs& a, hipStream_t s);
 template <typename T>
 hipError_t launch_dec_norm(const DecArgs& a, bool gather_inputs, int fold, const float* g,
                            float eps, T* Xn, hipStream_t s);
-hipError_t launch_dec_prep(const DecArgs& a, int fold, hipStream_t s);
-hipError_t launch_dec_update(const DecArgs& a, int fold, hipStream_t s);
+// prep and update also do the RMSNorm (gain, eps) of every slot row into Xn for the layer that
+// follows them.
+template <typename T>
+hipError_t launch_dec_prep(const DecArgs& a, int fold, const float* gain, float eps, T* Xn, hipStream_t s);
+template <typename T>
+hipError_t launch_dec_update(const DecArgs& a, int fold, const float* gain, float eps, T* Xn, hipStream_t s);
 hipError_t launch_dec_output(const DecArgs& a, int fold, hipStream_t s);
 template <typename T>
 hipError_t launch_dec_attn(const DecArgs& a, int kind, int j, hipStream_t s);
