@@ -577,6 +577,57 @@ hipError_t launch_dec_output(const DecArgs& a, int fold, hipStream_t s) {
 // Waves per (slot, KV head) workgroup: 16 where the LDS holds 16 waves' V tiles and
 // accumulators (bf16, up to 3 query heads per KV head), else 8; a context of n keys takes
 // ceil(n / (64 NW)) tiles per wave.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Scheduling fences with no code: use_now makes a value (and so its load) complete here;
+// opaque hides a value's origin, so arithmetic on it cannot be hoisted above this point.
+__device__ __forceinline__ void use_now(int v) { asm volatile("" ::"s"(v)); }
+__device__ __forceinline__ void use_now(long long v) { asm volatile("" ::"s"(v)); }
+__device__ __forceinline__ void use_now(const void* v) { asm volatile("" ::"s"(v)); }
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// One 16-byte direct-to-LDS load per lane: lane l's 16 bytes land at dst + 16 l.
+__device__ __forceinline__ void dma16(const uint4* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+
+// Issues the loads of one 64-key tile of a slot's layer stream: lane l's K row (key t0 + l) into
+// k, and the tile's V rows into the wave's LDS tile vt ([64][HD]) with direct-to-LDS 16-byte
+// loads (instruction q, lane l: chunk 64 q + l of the tile, i.e. key (64 q + l) / chunks-per-row).
+// Keys past nkeys (>= 1) re-read key nkeys - 1: every address is a cached row. All page numbers
+// are read first (one per lane and row set, however the rows fall into pages), so the row loads
+// wait for one page-table round trip in all and then issue back to back.
+template <typename T, int HD, int KT>
+__device__ __forceinline__ void issue_dec_tile(const DecArgs& a, const T* pool, const int* pt,
+                                               size_t vofs, int kvh, int t0, int nkeys, int lane,
+                                               uint4* k, T* vt) {
+  constexpr int CH = 16 / (int)sizeof(T), RCHUNKS = HD / CH, NQ = KT * RCHUNKS / 64;
+  const int ik = min(t0 + lane, nkeys - 1);
+  int iv[NQ], pv[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) iv[q] = min(t0 + (q * 64 + lane) / RCHUNKS, nkeys - 1);
+  int pk = pt[ik / a.P];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) pv[q] = pt[iv[q] / a.P];
+  // every page number in hand before the first row load: the compiler's wait for a register
+  // loaded before a direct-to-LDS load is a full drain, which would serialise the row loads
+  pk = opaque(pk);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) pv[q] = opaque(pv[q]);
+  const T* kr = pool + (size_t)pk * a.page_elems + ((size_t)kvh * a.P + ik % a.P) * HD;
+#pragma unroll
+  for (int c0 = 0; c0 < RCHUNKS; ++c0) k[c0] = *reinterpret_cast<const uint4*>(kr + c0 * CH);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int cc = (q * 64 + lane) % RCHUNKS;
+    const T* vr = pool + (size_t)pv[q] * a.page_elems + vofs + ((size_t)kvh * a.P + iv[q] % a.P) * HD;
+    dma16(reinterpret_cast<const uint4*>(vr + cc * CH), reinterpret_cast<char*>(vt + q * 64 * CH));
+  }
+}
+
 template <typename T, int G> constexpr int dec_attn_waves() { return sizeof(T) == 2 && G <= 3 ? 16 : 8; }
 
 template <typename T, int HD, int G, int NW = dec_attn_waves<T, G>()>
@@ -591,12 +642,27 @@ __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j
   __shared__ float sm[NW][G], sl[NW][G];
   __shared__ float sacc[NW][G][HD];
 
-  const int s = blockIdx.x, kvh = blockIdx.y;
-  if (s >= a.S) return;
-  const int part = kind == DL_FIRST ? a.sl_first[s] : kind == DL_LAST ? a.sl_exit[s] : a.sl_part[s];
+  const int s = blockIdx.x, kvh = blockIdx.y;       // the grid has one row per slot
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The slot's state in one round trip: flag, position, depth and every per-recursion count (the
+  // count this layer needs depends on the depth). The empty asm uses every value before the
+  // participation test, so the compiler cannot move the other loads behind it.
+  const int* flag = kind == DL_FIRST ? a.sl_first : kind == DL_LAST ? a.sl_exit : a.sl_part;
+  const int part = flag[s];
+  const int sbase = a.sl_base[s], spos = a.sl_pos[s], r = a.sl_depth[s];
+  int cnt[MOR_MAX_REC_DEV];
+#pragma unroll
+  for (int q = 0; q < MOR_MAX_REC_DEV; ++q) cnt[q] = a.sl_cnt[s * a.R + min(q, a.R - 1)];
+  use_now(part); use_now(sbase); use_now(spos); use_now(r);
+#pragma unroll
+  for (int q = 0; q < MOR_MAX_REC_DEV; ++q) use_now(cnt[q]);
+  // the arguments used before the first barrier, so their loads share the first round trip
+  use_now(a.n_s); use_now(a.P); use_now(a.pps); use_now(a.LS); use_now(a.nqkv); use_now(a.kv_share);
+  use_now(a.page_elems); use_now(a.ptab); use_now(a.pool); use_now(a.qkv); use_now(a.rope_cos);
+  use_now(a.kqkv);
   if (!part) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int pos = a.sl_base[s] + a.sl_pos[s], r = a.sl_depth[s];   // position in the sequence
+  const int pos = sbase + spos;                      // position in the sequence
   int ls_w, ls_r, idx_w, nkeys;
   if (kind == DL_FIRST || kind == DL_LAST) {
     ls_w = ls_r = (kind == DL_FIRST) ? 0 : 1;
@@ -606,12 +672,32 @@ __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j
     ls_w = -1;
     ls_r = layer_stream_shared(a, 1, j);
     idx_w = 0;
-    nkeys = a.sl_cnt[s * a.R + 0];
+    nkeys = cnt[0];
   } else {
     ls_w = ls_r = layer_stream_shared(a, r, j);
-    idx_w = a.sl_cnt[s * a.R + r - 1];
-    nkeys = idx_w;
+    int c = cnt[0];
+#pragma unroll
+    for (int q = 1; q < MOR_MAX_REC_DEV; ++q)
+      if (q == r - 1) c = cnt[q];
+    idx_w = c;
+    nkeys = c;
   }
+  T* pool = reinterpret_cast<T*>(a.pool);
+  const size_t vofs = (size_t)a.hkv * a.P * HD;
+  const int* pt = a.ptab + ((size_t)s * a.LS + ls_r) * a.pps;
+  // page of the appended key and value, read early by the threads that store them (a per-thread
+  // value, so nothing waits for it before the barrier)
+  const int page_w = (ls_w >= 0 && tid < 2 * HD) ? a.ptab[((size_t)s * a.LS + ls_w) * a.pps + idx_w / a.P] : 0;
+  T* svw = sv[wave];
+  // This wave's first tile is issued before the query/key/value fold below, so its page-table
+  // and row loads overlap the fold's: K rows into registers (lane = key), V rows into the
+  // wave's LDS tile by direct-to-LDS loads.
+  int t0 = wave * KT;
+  union KRow { uint4 u[RCHUNKS]; T e[RCHUNKS * CH]; } kc;
+  if (t0 < nkeys) issue_dec_tile<T, HD, KT>(a, pool, pt, vofs, kvh, t0, nkeys, lane, kc.u, svw);
+  // Query heads, key and value of the slot's token: the K-split partial sums added in split
+  // order, RoPE on q and k, rounded to the element type. Every load of a thread (both halves'
+  // partial sums and the rotation) is issued before any of them is used.
   const int half = HD / 2;
   const float* qkv = a.qkv + (size_t)s * a.nqkv;
   for (int i = tid; i < (G + 2) * HD; i += NW * 64) {
@@ -622,25 +708,20 @@ __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j
     else if (hh == G) base = qkv + a.nq + kvh * HD;
     else base = qkv + a.nq + a.nkv + kvh * HD;
     const size_t split = (size_t)64 * a.nqkv;     // partial sums of the K splits, added in order
+    const int f = c % half;
+    const float cs = a.rope_cos[pos * half + f], sn = a.rope_sin[pos * half + f];
     const float v0 = fold_splits(base[c], base + split + c, split, a.kqkv - 1);
     const float vp = fold_splits(base[pc], base + split + pc, split, a.kqkv - 1);
-    float v = v0;
-    if (hh <= G) {
-      const int f = c % half;
-      const float cs = a.rope_cos[pos * half + f], sn = a.rope_sin[pos * half + f];
-      v = c < half ? v * cs - vp * sn : v * cs + vp * sn;
-    }
-    v = to_f32(from_f32<T>(v));
+    const float rot = c < half ? v0 * cs - vp * sn : v0 * cs + vp * sn;
+    const float v = to_f32(from_f32<T>(hh <= G ? rot : v0));
     if (hh < G) sq[hh][c] = v;
     else if (hh == G) skn[c] = v;
     else svn[c] = v;
   }
   __syncthreads();
-  T* pool = reinterpret_cast<T*>(a.pool);
-  const size_t vofs = (size_t)a.hkv * a.P * HD;
   if (ls_w >= 0 && tid < 2 * HD) {
-    const int page = a.ptab[((size_t)s * a.LS + ls_w) * a.pps + idx_w / a.P];
-    T* dst = pool + (size_t)page * a.page_elems + ((size_t)kvh * a.P + idx_w % a.P) * HD;
+    const int pw = opaque(page_w);     // keeps the address arithmetic (and its wait) after the barrier
+    T* dst = pool + (size_t)pw * a.page_elems + ((size_t)kvh * a.P + idx_w % a.P) * HD;
     if (tid < HD) dst[tid] = from_f32<T>(skn[tid]);
     else dst[vofs + tid - HD] = from_f32<T>(svn[tid - HD]);
   }
@@ -660,35 +741,20 @@ __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j
       acc[hh] = lane_c ? svn[lane] : 0.f;
     }
   }
-  const int* pt = a.ptab + ((size_t)s * a.LS + ls_r) * a.pps;
-  T* svw = sv[wave];
-  for (int t0 = wave * KT; t0 < nkeys; t0 += NW * KT) {
+  for (; t0 < nkeys; t0 += NW * KT) {
     const int nt = min(KT, nkeys - t0);
-    // V rows of the tile -> LDS (16-byte chunks, consecutive lanes on consecutive chunks)
-    for (int cidx = lane; cidx < nt * RCHUNKS; cidx += 64) {
-      const int kk = cidx / RCHUNKS, cc = cidx % RCHUNKS;
-      const int ik = t0 + kk;
-      const T* vr = pool + (size_t)pt[ik / a.P] * a.page_elems + vofs + ((size_t)kvh * a.P + ik % a.P) * HD;
-      *reinterpret_cast<uint4*>(svw + kk * HD + cc * CH) = *reinterpret_cast<const uint4*>(vr + cc * CH);
-    }
     const int i = t0 + lane;
     const bool valid = i < nkeys;
     float sc[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) sc[hh] = 0.f;
     if (valid) {
-      const T* kr = pool + (size_t)pt[i / a.P] * a.page_elems + ((size_t)kvh * a.P + i % a.P) * HD;
-      union { uint4 u; T e[CH]; } kc[RCHUNKS];
 #pragma unroll
-      for (int c0 = 0; c0 < RCHUNKS; ++c0) kc[c0].u = *reinterpret_cast<const uint4*>(kr + c0 * CH);
+      for (int e = 0; e < RCHUNKS * CH; ++e) {
+        const float kv = to_f32(kc.e[e]);
 #pragma unroll
-      for (int c0 = 0; c0 < RCHUNKS; ++c0)
-#pragma unroll
-        for (int e = 0; e < CH; ++e) {
-          const float kv = to_f32(kc[c0].e[e]);
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) sc[hh] += sq[hh][c0 * CH + e] * kv;
-        }
+        for (int hh = 0; hh < G; ++hh) sc[hh] += sq[hh][e] * kv;
+      }
     }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
@@ -708,6 +774,8 @@ __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // the tile's V rows have landed in LDS (direct-to-LDS loads count as vector memory loads)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (lane_c) {
 #pragma unroll 8
       for (int kk = 0; kk < nt; ++kk) {
@@ -719,6 +787,11 @@ __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // the next tile of this wave (its V tile overwrites the one just read)
+    if (t0 + NW * KT < nkeys) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue_dec_tile<T, HD, KT>(a, pool, pt, vofs, kvh, t0 + NW * KT, nkeys, lane, kc.u, svw);
+    }
   }
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
