@@ -42,6 +42,36 @@ __device__ __forceinline__ int layer_stream_shared(const DecArgs& a, int r, int 
   return 2 + (r - 1) * a.n_s + (j - 1);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Scheduling fences with no code: use_now makes a value (and so its load) complete here;
+// opaque hides a value's origin, so arithmetic on it cannot be hoisted above this point.
+__device__ __forceinline__ void use_now(int v) { asm volatile("" ::"s"(v)); }
+__device__ __forceinline__ void use_now(long long v) { asm volatile("" ::"s"(v)); }
+__device__ __forceinline__ void use_now(const void* v) { asm volatile("" ::"s"(v)); }
+__device__ __forceinline__ void use_now(int a, int b, int c) { asm volatile("" ::"s"(a), "s"(b), "s"(c)); }
+__device__ __forceinline__ void use_now(int a, int b, int c, int d, int e) {
+  asm volatile("" ::"s"(a), "s"(b), "s"(c), "s"(d), "s"(e));
+}
+__device__ __forceinline__ void use_now(int a, int b, int c, int d, float e) {
+  asm volatile("" ::"s"(a), "s"(b), "s"(c), "s"(d), "s"(e));
+}
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Loads one field from each 64-byte line of the decode arguments together, so the kernel's
+// later argument reads hit the scalar cache instead of each costing a round trip.
+__device__ __forceinline__ void touch_args(const DecArgs& a) {
+  asm volatile("" ::"s"(a.S), "s"(a.sl_req), "s"(a.ptab), "s"(a.X), "s"(a.px), "s"(a.stats));
+}
+
+// One 16-byte direct-to-LDS load per lane: lane l's 16 bytes land at dst + 16 l.
+__device__ __forceinline__ void dma16(const uint4* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ scheduler (one wave)
@@ -287,38 +317,51 @@ __device__ __forceinline__ void norm_row_as_is(const float4* x, const float* gai
   row_norm_store<T>(v, gg, ss, nc, d, eps, red, out);
 }
 
-template <typename T>
-__global__ __launch_bounds__(ROW_THREADS) void k_dec_norm(DecArgs a, int gather, int fold,
-                                                          const float* __restrict__ g, float eps,
-                                                          T* __restrict__ Xn) {
+template <typename T, bool GATHER>
+__global__ __launch_bounds__(ROW_THREADS) void k_dec_norm(DecArgs a, int fold, const float* __restrict__ g,
+                                                          float eps, T* __restrict__ Xn) {
   __shared__ float red[4];
+  touch_args(a);
   const int s = blockIdx.x, t = threadIdx.x;
   const int d = a.d, nc = d / 4;
   float4* x = reinterpret_cast<float4*>(a.X + (size_t)s * d);
-  const bool load_in = gather && a.sl_first[s];
-  const float4* src = load_in ? reinterpret_cast<const float4*>(
-                                    a.inputs + (size_t)(a.req_off[a.sl_req[s]] + a.sl_pos[s]) * d)
-                              : nullptr;
-  // the gains are loaded with the row, so the reduction is the only wait after the loads
   const float4* g4 = reinterpret_cast<const float4*>(g);
   float4 v[ROW_CHUNKS], gg[ROW_CHUNKS];
+  if (GATHER) {
+    // the slot's flag, request and position in one round trip, then the request's row offset
+    const int first = a.sl_first[s], req = a.sl_req[s], pos = a.sl_pos[s];
+    use_now(first, req, pos);
+    const float4* src = (first && req >= 0)
+                            ? reinterpret_cast<const float4*>(a.inputs + (size_t)(a.req_off[req] + pos) * d)
+                            : nullptr;
+#pragma unroll
+    for (int u = 0; u < ROW_CHUNKS; ++u) {
+      const int c = t + u * ROW_THREADS;
+      v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < nc) {
+        if (src) v[u] = src[c];
+        gg[u] = g4[c];
+      }
+    }
+  } else {
+    // the row, the partial sums and the gains all in one round trip
+    const float4* px = reinterpret_cast<const float4*>(a.px + (size_t)s * d);
+#pragma unroll
+    for (int u = 0; u < ROW_CHUNKS; ++u) {
+      const int c = t + u * ROW_THREADS;
+      v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < nc) {
+        gg[u] = g4[c];
+        v[u] = fold_splits(x[c], px + c, (size_t)64 * d / 4, fold);
+      }
+    }
+  }
   float ss = 0.f;
 #pragma unroll
   for (int u = 0; u < ROW_CHUNKS; ++u) {
     const int c = t + u * ROW_THREADS;
-    float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c < nc) {
-      gg[u] = g4[c];
-      if (gather) {
-        if (load_in) w = src[c];
-      } else {
-        w = fold_splits(x[c], reinterpret_cast<const float4*>(a.px + (size_t)s * d) + c,
-                        (size_t)64 * d / 4, fold);
-      }
-      if (gather || fold) x[c] = w;
-    }
-    v[u] = w;
-    ss += sq4(w);
+    if (c < nc && (GATHER || fold)) x[c] = v[u];
+    ss += sq4(v[u]);
   }
   row_norm_store<T>(v, gg, ss, nc, d, eps, red, Xn + (size_t)s * d);
 }
@@ -327,8 +370,10 @@ template <typename T>
 hipError_t launch_dec_norm(const DecArgs& a, bool gather_inputs, int fold, const float* g,
                            float eps, T* Xn, hipStream_t s) {
   if (a.d > 4 * ROW_CHUNKS * ROW_THREADS || fold < 0 || fold > kMaxSplits) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_dec_norm<T>), dim3(a.S), dim3(ROW_THREADS), 0, s, a, gather_inputs ? 1 : 0,
-                     fold, g, eps, Xn);
+  if (gather_inputs)
+    hipLaunchKernelGGL((k_dec_norm<T, true>), dim3(a.S), dim3(ROW_THREADS), 0, s, a, 0, g, eps, Xn);
+  else
+    hipLaunchKernelGGL((k_dec_norm<T, false>), dim3(a.S), dim3(ROW_THREADS), 0, s, a, fold, g, eps, Xn);
   return hipGetLastError();
 }
 template hipError_t launch_dec_norm<float>(const DecArgs&, bool, int, const float*, float, float*, hipStream_t);
@@ -359,10 +404,12 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_prep(DecArgs a, int fold, c
                                                           float eps, T* __restrict__ Xn) {
   __shared__ float prod[ROW_MAX];
   __shared__ float red[4];
+  touch_args(a);
   const int s = blockIdx.x, t = threadIdx.x;
-  // the slot's state is read in one go (independent loads) before the participation test
+  // the slot's state in one round trip, before the participation test
   const int part = a.sl_part[s], r = a.sl_depth[s], first = a.sl_first[s];
   const int req = a.sl_req[s], pos = a.sl_pos[s];
+  use_now(part, r, first, req, pos);
   const int d = a.d, nc = d / 4;
   float4* __restrict__ x = reinterpret_cast<float4*>(a.X + (size_t)s * d);
   T* out = Xn + (size_t)s * d;
@@ -374,11 +421,11 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_prep(DecArgs a, int fold, c
   const float4* __restrict__ w = reinterpret_cast<const float4*>(a.router_w + (size_t)(r - 1) * d);
   const float4* __restrict__ px = reinterpret_cast<const float4*>(a.px + (size_t)s * d);
   const float4* g4 = reinterpret_cast<const float4*>(gain);
-  const int tok = a.req_off[req] + pos;
-  float4* __restrict__ dump = (first && a.h_dump)
-                                  ? reinterpret_cast<float4*>(a.h_dump + ((size_t)tok * (a.R + 1)) * d)
-                                  : nullptr;
-  // all loads first, then the stores (a store to x or hs would otherwise order later loads behind it)
+  // the request's row offset and the router bias are only needed at the end: read now, used late
+  const int roff = a.req_off[req];
+  const float bias = a.router_b[r - 1];
+  // all loads first (both the folded first-layer output and the carried state, so no branch
+  // separates them), then the stores (a store to x or hs would order later loads behind it)
   float4 h[ROW_CHUNKS], wv[ROW_CHUNKS], gg[ROW_CHUNKS];
 #pragma unroll
   for (int u = 0; u < ROW_CHUNKS; ++u) {
@@ -387,7 +434,11 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_prep(DecArgs a, int fold, c
     if (c < nc) {
       wv[u] = w[c];
       gg[u] = g4[c];
-      h[u] = first ? fold_splits(x[c], px + c, (size_t)64 * d / 4, fold) : hs[c];
+      const float4 hv = hs[c];
+      const float4 fv = fold_splits(x[c], px + c, (size_t)64 * d / 4, fold);
+      // component-wise: a select of whole float4 values is turned into an indexed private array
+      h[u] = make_float4(first ? fv.x : hv.x, first ? fv.y : hv.y, first ? fv.z : hv.z,
+                         first ? fv.w : hv.w);
     }
   }
   float ss = 0.f;
@@ -397,7 +448,6 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_prep(DecArgs a, int fold, c
     if (c < nc) {
       if (first) hs[c] = h[u];             // the folded first-layer output is the state...
       x[c] = h[u];                         // ...and the shared block's input
-      if (dump) dump[c] = h[u];
       prod[4 * c + 0] = mul_rn(h[u].x, wv[u].x);
       prod[4 * c + 1] = mul_rn(h[u].y, wv[u].y);
       prod[4 * c + 2] = mul_rn(h[u].z, wv[u].z);
@@ -406,8 +456,17 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_prep(DecArgs a, int fold, c
     ss += sq4(h[u]);
   }
   row_norm_store<T>(h, gg, ss, nc, d, eps, red, out);   // its barriers also publish prod
+  const int tok = opaque(roff) + pos;
+  if (first && a.h_dump) {
+    float4* dump = reinterpret_cast<float4*>(a.h_dump + ((size_t)tok * (a.R + 1)) * d);
+#pragma unroll
+    for (int u = 0; u < ROW_CHUNKS; ++u) {
+      const int c = t + u * ROW_THREADS;
+      if (c < nc) dump[c] = h[u];
+    }
+  }
   if (t >= WAVE) return;
-  const float z = row_logit_fixed(prod, d, a.router_b[r - 1]);
+  const float z = row_logit_fixed(prod, d, bias);
   if (t == 0) {
     if (z != z) atomicOr(a.err, (unsigned)ERR_NAN_LOGIT);
     a.gate[s] = a.unit_gate ? -1.f : 1.f / (1.f + __expf(-z));
@@ -438,9 +497,12 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_update(DecArgs a, int fold,
                                                             float eps, T* __restrict__ Xn) {
   __shared__ float prod[ROW_MAX];
   __shared__ float red[4];
+  touch_args(a);
   const int s = blockIdx.x, t = threadIdx.x;
+  // the slot's state in one round trip, before the participation test
   const int part = a.sl_part[s], r = a.sl_depth[s], req = a.sl_req[s], pos = a.sl_pos[s];
   const float g = a.gate[s];
+  use_now(part, r, req, pos, g);
   const int d = a.d, nc = d / 4;
   float4* __restrict__ x = reinterpret_cast<float4*>(a.X + (size_t)s * d);
   T* out = Xn + (size_t)s * d;
@@ -451,11 +513,14 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_update(DecArgs a, int fold,
   float4* __restrict__ hs = reinterpret_cast<float4*>(a.Hs + (size_t)s * d);
   const float4* __restrict__ px = reinterpret_cast<const float4*>(a.px + (size_t)s * d);
   const float4* g4 = reinterpret_cast<const float4*>(gain);
-  const int tok = a.req_off[req] + pos;
+  // the next recursion's router row (a valid row even after the last recursion, unused there),
+  // and what is only needed at the end (row offset, bias, recursion count): read now, used late
+  const bool next = r < a.R;
   const float4* __restrict__ w =
-      (r < a.R) ? reinterpret_cast<const float4*>(a.router_w + (size_t)r * d) : nullptr;
-  float4* __restrict__ dump =
-      a.h_dump ? reinterpret_cast<float4*>(a.h_dump + ((size_t)tok * (a.R + 1) + r) * d) : nullptr;
+      reinterpret_cast<const float4*>(a.router_w + (size_t)min(r, a.R - 1) * d);
+  const int roff = a.req_off[req];
+  const float bias = a.router_b[min(r, a.R - 1)];
+  const int done_r = a.sl_cnt[s * a.R + r - 1];
   // all loads first, then the stores
   float4 hn[ROW_CHUNKS], wv[ROW_CHUNKS], gg[ROW_CHUNKS];
 #pragma unroll
@@ -463,10 +528,10 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_update(DecArgs a, int fold,
     const int c = t + u * ROW_THREADS;
     hn[u] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (c < nc) {
-      const float4 xv = fold_splits(x[c], px + c, (size_t)64 * d / 4, fold);
-      const float4 hv = hs[c];
       gg[u] = g4[c];
-      wv[u] = w ? w[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      wv[u] = w[c];
+      const float4 hv = hs[c];
+      const float4 xv = fold_splits(x[c], px + c, (size_t)64 * d / 4, fold);
       hn[u] = make_float4(gate_mix(g, xv.x, hv.x), gate_mix(g, xv.y, hv.y), gate_mix(g, xv.z, hv.z),
                           gate_mix(g, xv.w, hv.w));
     }
@@ -478,8 +543,7 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_update(DecArgs a, int fold,
     if (c < nc) {
       hs[c] = hn[u];
       x[c] = hn[u];
-      if (dump) dump[c] = hn[u];
-      if (w) {
+      if (next) {
         prod[4 * c + 0] = mul_rn(hn[u].x, wv[u].x);
         prod[4 * c + 1] = mul_rn(hn[u].y, wv[u].y);
         prod[4 * c + 2] = mul_rn(hn[u].z, wv[u].z);
@@ -489,10 +553,19 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_update(DecArgs a, int fold,
     ss += sq4(hn[u]);
   }
   row_norm_store<T>(hn, gg, ss, nc, d, eps, red, out);  // its barriers also publish prod
+  const int tok = opaque(roff) + pos;
+  if (a.h_dump) {
+    float4* dump = reinterpret_cast<float4*>(a.h_dump + ((size_t)tok * (a.R + 1) + r) * d);
+#pragma unroll
+    for (int u = 0; u < ROW_CHUNKS; ++u) {
+      const int c = t + u * ROW_THREADS;
+      if (c < nc) dump[c] = hn[u];
+    }
+  }
   if (t >= WAVE) return;
   bool leave = true;
-  if (w) {
-    const float p = row_logit_fixed(prod, d, a.router_b[r]);
+  if (next) {
+    const float p = row_logit_fixed(prod, d, bias);
     leave = !(p > 0.f);
     if (t == 0) {
       if (p != p) atomicOr(a.err, (unsigned)ERR_NAN_LOGIT);
@@ -500,7 +573,7 @@ __global__ __launch_bounds__(ROW_THREADS) void k_dec_update(DecArgs a, int fold,
     }
   }
   if (t == 0) {
-    a.sl_cnt[s * a.R + r - 1] += 1;
+    a.sl_cnt[s * a.R + r - 1] = done_r + 1;
     if (leave) {
       a.sl_exit[s] = 1;
       a.exit_depth[tok] = (signed char)r;
@@ -574,26 +647,6 @@ hipError_t launch_dec_output(const DecArgs& a, int fold, hipStream_t s) {
 // Waves take 64-key tiles in turn. Scores: lane = key (its K row against the G query heads held
 // in LDS). Values: the tile's V rows are copied into LDS with 16-byte loads, then lane = head-dim
 // element accumulates over the tile's keys. The waves' partial results are merged in wave order.
-// Waves per (slot, KV head) workgroup: 16 where the LDS holds 16 waves' V tiles and
-// accumulators (bf16, up to 3 query heads per KV head), else 8; a context of n keys takes
-// ceil(n / (64 NW)) tiles per wave.
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Scheduling fences with no code: use_now makes a value (and so its load) complete here;
-// opaque hides a value's origin, so arithmetic on it cannot be hoisted above this point.
-__device__ __forceinline__ void use_now(int v) { asm volatile("" ::"s"(v)); }
-__device__ __forceinline__ void use_now(long long v) { asm volatile("" ::"s"(v)); }
-__device__ __forceinline__ void use_now(const void* v) { asm volatile("" ::"s"(v)); }
-__device__ __forceinline__ int opaque(int v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
-// One 16-byte direct-to-LDS load per lane: lane l's 16 bytes land at dst + 16 l.
-__device__ __forceinline__ void dma16(const uint4* src, char* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
-}
-
 // Issues the loads of one 64-key tile of a slot's layer stream: lane l's K row (key t0 + l) into
 // k, and the tile's V rows into the wave's LDS tile vt ([64][HD]) with direct-to-LDS 16-byte
 // loads (instruction q, lane l: chunk 64 q + l of the tile, i.e. key (64 q + l) / chunks-per-row).
@@ -628,9 +681,15 @@ __device__ __forceinline__ void issue_dec_tile(const DecArgs& a, const T* pool, 
   }
 }
 
-template <typename T, int G> constexpr int dec_attn_waves() { return sizeof(T) == 2 && G <= 3 ? 16 : 8; }
+// Waves per (slot, KV head) workgroup: 16 where the LDS holds 16 waves' V tiles and
+// accumulators (bf16, up to 3 query heads per KV head) and the registers of 16 waves suffice
+// (head dim 64, or a single query head), else 8; a context of n keys takes ceil(n / (64 NW))
+// tiles per wave.
+template <typename T, int HD, int G> constexpr int dec_attn_waves() {
+  return sizeof(T) == 2 && G <= 3 && (HD == 64 || G == 1) ? 16 : 8;
+}
 
-template <typename T, int HD, int G, int NW = dec_attn_waves<T, G>()>
+template <typename T, int HD, int G, int NW = dec_attn_waves<T, HD, G>()>
 __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j) {
   constexpr int KT = 64;
   constexpr int CH = 16 / (int)sizeof(T);            // elements per 16-byte chunk
@@ -642,6 +701,7 @@ __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j
   __shared__ float sm[NW][G], sl[NW][G];
   __shared__ float sacc[NW][G][HD];
 
+  touch_args(a);
   const int s = blockIdx.x, kvh = blockIdx.y;       // the grid has one row per slot
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -734,8 +794,8 @@ __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j
   if (wave == 0 && ls_w >= 0) {            // the new key: p = exp2(0) = 1
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      float dot = 0.f;
-      for (int c = 0; c < HD; ++c) dot += sq[hh][c] * skn[c];
+      // lane c forms q[c] k[c], the wave sums them (a shuffle tree, not a 64-long chain)
+      const float dot = wave_sum(lane_c ? sq[hh][lane] * skn[lane] : 0.f);
       m[hh] = dot * sl2;
       l[hh] = 1.f;
       acc[hh] = lane_c ? svn[lane] : 0.f;
@@ -799,20 +859,21 @@ __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j
     if (lane_c) sacc[wave][hh][lane] = acc[hh];
   }
   __syncthreads();
-  if (wave == 0 && lane_c) {
+  // Wave hh merges query head hh, in wave order, over the waves that held keys (wave 0 and the
+  // waves with a tile; the others hold m = -inf, l = 0, acc = 0 and would add exact zeros).
+  const int nw_used = min(NW, max(1, (nkeys + KT - 1) / KT));
+  if (wave < G && lane_c) {
+    const int hh = wave;
     T* out = reinterpret_cast<T*>(a.o) + (size_t)s * a.nq;
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float M = -INFINITY;
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w][hh]);
-      float L = 0.f, o = 0.f;
-      for (int w = 0; w < NW; ++w) {
-        const float f = (sm[w][hh] == -INFINITY) ? 0.f : exp2f(sm[w][hh] - M);
-        L += sl[w][hh] * f;
-        o += sacc[w][hh][lane] * f;
-      }
-      out[(kvh * G + hh) * HD + lane] = from_f32<T>(o / L);
+    float M = -INFINITY;
+    for (int w = 0; w < nw_used; ++w) M = fmaxf(M, sm[w][hh]);
+    float L = 0.f, o = 0.f;
+    for (int w = 0; w < nw_used; ++w) {
+      const float f = (sm[w][hh] == -INFINITY) ? 0.f : exp2f(sm[w][hh] - M);
+      L += sl[w][hh] * f;
+      o += sacc[w][hh][lane] * f;
     }
+    out[(kvh * G + hh) * HD + lane] = from_f32<T>(o / L);
   }
 }
 
@@ -820,10 +881,10 @@ template <typename T, int HD>
 static hipError_t dec_attn_g(const DecArgs& a, int kind, int j, hipStream_t s) {
   dim3 grid(a.S, a.hkv);
   switch (a.hq / a.hkv) {
-    case 1: hipLaunchKernelGGL((k_dec_attn<T, HD, 1>), grid, dim3(dec_attn_waves<T, 1>() * 64), 0, s, a, kind, j); break;
-    case 2: hipLaunchKernelGGL((k_dec_attn<T, HD, 2>), grid, dim3(dec_attn_waves<T, 2>() * 64), 0, s, a, kind, j); break;
-    case 3: hipLaunchKernelGGL((k_dec_attn<T, HD, 3>), grid, dim3(dec_attn_waves<T, 3>() * 64), 0, s, a, kind, j); break;
-    case 4: hipLaunchKernelGGL((k_dec_attn<T, HD, 4>), grid, dim3(dec_attn_waves<T, 4>() * 64), 0, s, a, kind, j); break;
+    case 1: hipLaunchKernelGGL((k_dec_attn<T, HD, 1>), grid, dim3(dec_attn_waves<T, HD, 1>() * 64), 0, s, a, kind, j); break;
+    case 2: hipLaunchKernelGGL((k_dec_attn<T, HD, 2>), grid, dim3(dec_attn_waves<T, HD, 2>() * 64), 0, s, a, kind, j); break;
+    case 3: hipLaunchKernelGGL((k_dec_attn<T, HD, 3>), grid, dim3(dec_attn_waves<T, HD, 3>() * 64), 0, s, a, kind, j); break;
+    case 4: hipLaunchKernelGGL((k_dec_attn<T, HD, 4>), grid, dim3(dec_attn_waves<T, HD, 4>() * 64), 0, s, a, kind, j); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
