@@ -290,7 +290,17 @@ __global__ __launch_bounds__(256) void k_gather(const float* __restrict__ H, int
   const int src = b * T + pos;
   const float4* hs = reinterpret_cast<const float4*>(H + (size_t)src * d);
   float4* xd = reinterpret_cast<float4*>(X + (size_t)i * d);
-  for (int c = lane; c < d / 4; c += WAVE) xd[c] = hs[c];
+  const int n4 = d / 4;
+  if (n4 <= 4 * WAVE) {                  // rows up to 1024: every load before the first store
+    float4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = hs[min(lane + k * WAVE, n4 - 1)];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (lane + k * WAVE < n4) xd[lane + k * WAVE] = v[k];
+  } else {
+    for (int c = lane; c < n4; c += WAVE) xd[c] = hs[c];
+  }
   if (lane == 0) {
     rowpos[i] = pos;
     rowsrc[i] = src;
@@ -315,7 +325,10 @@ hipError_t launch_gather(const float* H, int d, const int* act, const int* meta,
 }
 
 // One wave per compacted row: H[src] <- H[src] + g (X[i] - H[src]) (g < 0: H[src] <- X[i]),
-// then, if w_next is given, the next recursion's router logit of the updated row (fixed order).
+// then, if w_next is given, the next recursion's router logit of the updated row (fixed order:
+// lane l sums elements l, l + 64, ... ascending). With CH > 0 (d <= 64 CH) every element of the
+// lane is loaded before any is used (one memory round trip per row); CH = 0 loops.
+template <int CH>
 __global__ __launch_bounds__(256) void k_scatter(float* __restrict__ H, const float* __restrict__ X,
                                                  int d, const int* __restrict__ meta,
                                                  const int* __restrict__ rowsrc,
@@ -331,11 +344,31 @@ __global__ __launch_bounds__(256) void k_scatter(float* __restrict__ H, const fl
   float* h = H + (size_t)src * d;
   const float* x = X + (size_t)i * d;
   float p = 0.f;
-  for (int c = lane; c < d; c += WAVE) {
-    const float hv = h[c], xv = x[c];
-    const float hn = (g < 0.f) ? xv : hv + g * (xv - hv);
-    h[c] = hn;
-    if (w_next) p = add_rn(p, mul_rn(hn, w_next[c]));
+  if constexpr (CH > 0) {
+    float hv[CH], xv[CH], wv[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int c = min(lane + k * WAVE, d - 1);    // loads clamped in range, stores guarded
+      hv[k] = h[c];
+      xv[k] = x[c];
+      wv[k] = w_next ? w_next[c] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int c = lane + k * WAVE;
+      if (c < d) {
+        const float hn = (g < 0.f) ? xv[k] : hv[k] + g * (xv[k] - hv[k]);
+        h[c] = hn;
+        if (w_next) p = add_rn(p, mul_rn(hn, wv[k]));
+      }
+    }
+  } else {
+    for (int c = lane; c < d; c += WAVE) {
+      const float hv = h[c], xv = x[c];
+      const float hn = (g < 0.f) ? xv : hv + g * (xv - hv);
+      h[c] = hn;
+      if (w_next) p = add_rn(p, mul_rn(hn, w_next[c]));
+    }
   }
   if (w_next) {
     p = fold_fixed(p);
@@ -348,8 +381,11 @@ hipError_t launch_scatter(float* H, const float* X, int d, const int* meta, int 
                           const int* rowsrc, const float* gate, const float* w_next,
                           const float* bias_next, float* z_next, hipStream_t s) {
   if (m_upper <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_scatter, dim3((m_upper + 3) / 4), dim3(256), 0, s, H, X, d, meta, rowsrc,
-                     gate, w_next, bias_next, z_next);
+  const dim3 grid((m_upper + 3) / 4), blk(256);
+  if (d <= 16 * WAVE)
+    hipLaunchKernelGGL(k_scatter<16>, grid, blk, 0, s, H, X, d, meta, rowsrc, gate, w_next, bias_next, z_next);
+  else
+    hipLaunchKernelGGL(k_scatter<0>, grid, blk, 0, s, H, X, d, meta, rowsrc, gate, w_next, bias_next, z_next);
   return hipGetLastError();
 }
 
