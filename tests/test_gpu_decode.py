@@ -123,6 +123,20 @@ def test_decode_small_f32_free_running():
     model.close()
 
 
+def test_decode_wide_rows_f32_free_running():
+    """d_model 1088 (> 1024 = one float4 per thread of a 256-thread row workgroup): every row
+    kernel takes its second chunk; 32-token pages (two pages per 64-key attention tile)."""
+    cfg = workload.get_config("small_thr_bf16", dtype="f32", d_model=1088)
+    model, W, lens = _setup(cfg, slots=5, page=32)
+    inputs = workload.make_decode_inputs(cfg, lens)
+    res = _run(model, cfg, lens, inputs)
+    _check_routing(cfg, W, res, lens)
+    worst = _compare(cfg, W, res, lens, inputs, teacher=False)
+    say(f"[gpu] decode f32 d 1088: worst rel err {worst:.2e}, "
+        f"depth histogram {np.bincount(res['depth'], minlength=cfg.n_rec + 1)[1:]}")
+    model.close()
+
+
 def test_decode_small_bf16_teacher_forced():
     cfg = workload.get_config("small_thr_bf16")
     model, W, lens = _setup(cfg, slots=5)

@@ -55,6 +55,12 @@ def test_small_f32_ragged_free_running():
     _compare_prefill(workload.get_config("small_f32"))
 
 
+def test_wide_rows_f32_free_running():
+    """d_model 1088 (> 1024): the row kernels' general paths (RMSNorm, gather and scatter loop
+    over a row instead of holding it in registers); attention width 128 differs from d_model."""
+    _compare_prefill(workload.get_config("small_f32", d_model=1088, batch=2, seq=96))
+
+
 def test_small_f32_unit_gate_full_capacity():
     """Capacity 1 everywhere with unit gating: the fixed-depth recursive model."""
     _compare_prefill(workload.get_config("small_f32", gate_mode="unit", cap_num=(3, 3, 3)))
