@@ -8,8 +8,10 @@
 //  - LDS rows are 128 bytes (64 bf16 of K) with the 16-byte chunks XOR-swizzled by
 //    (row >> 1) & 7, so the ds_read_b128 fragment reads of 16 consecutive rows hit 16 distinct
 //    bank groups;
-//  - 4 waves in 2 x 2, each owning a (BN/2) x (BM/2) block of the output: 128 x 128 at the
-//    256 x 256 tile, i.e. 64 FLOP per LDS byte read, enough to keep the matrix cores fed;
+//  - 4 waves in 2 x 2, each owning a (BN/2) x (BM/2) block of the output (BN weight rows x BM
+//    activation rows per tile: 128 x 128, 192 x 128 or 128 x 192 at two workgroups per CU,
+//    256 x 128 and 256 x 256 at one); the tile is chosen per launch from the number of rounds
+//    of resident workgroups it needs (choose_tile below);
 //  - two LDS stages: the loads of step k+1 are in flight while step k is multiplied;
 //  - workgroups are renumbered so that the ones sharing an activation tile land on one XCD
 //    (the hardware deals workgroups round-robin over the 8 XCDs, each with its own L2).
@@ -245,7 +247,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(const bf16* __restrict__ A
 
 namespace {
 
-int g_forced_tile = -1;   // tuning override from MOR_GEMM_TILE ("256x256", "256x128", "128x128")
 int g_group_m = -1;       // tuning override of the tile-order group (MOR_GEMM_GROUP_M)
 
 int group_m() {
@@ -256,16 +257,17 @@ int group_m() {
   return g_group_m;
 }
 
+// Tile override MOR_GEMM_TILE ("128x128", "192x128", "128x192", "256x128", "256x256"); read at
+// every launch (a getenv per projection), so a process can change it between calls.
 int forced_tile() {
-  if (g_forced_tile == -1) {
-    g_forced_tile = 0;
-    if (const char* s = getenv("MOR_GEMM_TILE")) {
-      if (!strcmp(s, "256x256")) g_forced_tile = 1;
-      else if (!strcmp(s, "256x128")) g_forced_tile = 2;
-      else if (!strcmp(s, "128x128")) g_forced_tile = 3;
-    }
-  }
-  return g_forced_tile;
+  const char* s = getenv("MOR_GEMM_TILE");
+  if (!s) return 0;
+  if (!strcmp(s, "256x256")) return 1;
+  if (!strcmp(s, "256x128")) return 2;
+  if (!strcmp(s, "128x128")) return 3;
+  if (!strcmp(s, "192x128")) return 4;
+  if (!strcmp(s, "128x192")) return 5;
+  return 0;
 }
 
 template <int BN, int BM>
@@ -283,11 +285,40 @@ hipError_t launch_cfg(int epi, const bf16* A, const bf16* W, int N, int K, int m
   return hipGetLastError();
 }
 
-// Relative cost of one tile (matrix-core time at the tile's measured efficiency: the 128 x 128
-// tile runs two workgroups per CU and hides latency best on these shapes).
-double tile_cost(int bn, int bm) {
-  const double eff = (bn == 128 && bm == 128) ? 1.0 : (bn == 256 && bm == 256) ? 0.93 : 0.85;
-  return (double)bn * bm / eff;
+// One epilogue only (tile shapes the QKV epilogue cannot use).
+template <int BN, int BM, int EPI>
+hipError_t launch_cfg_rs(const bf16* A, const bf16* W, int N, int K, int m_upper, const int* meta,
+                         const GemmEpi& ep, hipStream_t s) {
+  const int tn = (N + BN - 1) / BN, tm = (m_upper + BM - 1) / BM;
+  const int nblk = tn * tm;
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI>), dim3(nblk), dim3(256), 0, s, A, W, N, K, tn, group_m(), meta, ep);
+  return hipGetLastError();
+}
+
+// Tile choice. A launch runs in rounds of as many tiles as fit on the chip at once (256 CUs x
+// workgroups per CU); a round costs about the same whatever the tile count in it, so the
+// estimate is rounds x the cost of one round of that tile relative to 128 x 128. Measured on
+// the 360M-shape projections: a round of 192 x 128 or 128 x 192 tiles (1.5x the work) costs
+// about 1.25 rounds of 128 x 128, the larger tiles reusing each LDS byte more. The 256-wide
+// tiles (one workgroup per CU) never won on these shapes and are left to MOR_GEMM_TILE.
+struct TileCfg {
+  int bn, bm, per_cu;
+  double round_cost;
+};
+constexpr TileCfg kTiles[] = {{128, 128, 2, 1.0}, {192, 128, 2, 1.25}, {128, 192, 2, 1.25}};
+
+int choose_tile(int epi, int N, int m_upper) {
+  int best = 0;
+  double best_t = 1e300;
+  for (int c = 0; c < 3; ++c) {
+    if (kTiles[c].bn == 192 && epi == EPI_QKV) continue;   // the QKV epilogue needs 64-wide halves
+    const long tiles = (long)((N + kTiles[c].bn - 1) / kTiles[c].bn) * ((m_upper + kTiles[c].bm - 1) / kTiles[c].bm);
+    const long slots = 256L * kTiles[c].per_cu;
+    const double t = (double)((tiles + slots - 1) / slots) * kTiles[c].round_cost;
+    if (t < best_t - 1e-9) { best_t = t; best = c; }
+  }
+  return best == 0 ? 3 : best == 1 ? 4 : 5;
 }
 
 }  // namespace
@@ -297,20 +328,17 @@ hipError_t launch_gemm<bf16>(int epi, const bf16* A, const bf16* W, int N, int K
                              const int* meta, const GemmEpi& ep, hipStream_t s) {
   if (K % 64 || N % 64) return hipErrorInvalidValue;
   int choice = forced_tile();
-  if (choice == 0) {
-    // pick the tile with the least estimated time: whole waves of 256 workgroups x tile cost
-    const int cfgs[3][2] = {{256, 256}, {256, 128}, {128, 128}};
-    double best = 1e300;
-    for (int c = 0; c < 3; ++c) {
-      const long tiles = (long)((N + cfgs[c][0] - 1) / cfgs[c][0]) * ((m_upper + cfgs[c][1] - 1) / cfgs[c][1]);
-      const double waves = (double)((tiles + 255) / 256);
-      const double t = waves * tile_cost(cfgs[c][0], cfgs[c][1]);
-      if (t < best) { best = t; choice = c + 1; }
-    }
-  }
+  if (choice == 0) choice = choose_tile(epi, N, m_upper);
+  // 192-wide weight tiles: residual and SwiGLU epilogues only (the QKV epilogue pairs the two
+  // halves of a 64-wide head inside one wave's 64-column share)
+  if (choice == 4 && epi == EPI_QKV) choice = 3;
   switch (choice) {
     case 1: return launch_cfg<256, 256>(epi, A, W, N, K, m_upper, meta, ep, s);
     case 2: return launch_cfg<256, 128>(epi, A, W, N, K, m_upper, meta, ep, s);
+    case 4:
+      if (epi == EPI_RESID) return launch_cfg_rs<192, 128, EPI_RESID>(A, W, N, K, m_upper, meta, ep, s);
+      return launch_cfg_rs<192, 128, EPI_SWIGLU>(A, W, N, K, m_upper, meta, ep, s);
+    case 5: return launch_cfg<128, 192>(epi, A, W, N, K, m_upper, meta, ep, s);
     default: return launch_cfg<128, 128>(epi, A, W, N, K, m_upper, meta, ep, s);
   }
 }

@@ -324,7 +324,7 @@ def main():
     peak = PEAK_BF16 if cfg.dtype == "bf16" else PEAK_FP32
     achieved = k_flops_per_launch / k_avg_s / 1e12 if k_flops_per_launch else None
     traffic = traffic_from_profile(kind, cfg.name)
-    roofline = {"bound": "mfma", "kernel": f"k_gemm<bf16,128,128,SWIGLU> ({kind} projection)",
+    roofline = {"bound": "mfma", "kernel": f"k_gemm_bf16, SwiGLU epilogue ({kind} projection; tile chosen per launch)",
                 "achieved": achieved, "peak": peak / 1e12, "unit": "TFLOP/s",
                 "frac": (achieved * 1e12 / peak) if achieved else None, "traffic": traffic,
                 "avg_launch_us": k_avg_s * 1e6, "launches_timed": k_n,
