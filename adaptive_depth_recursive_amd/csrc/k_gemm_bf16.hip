@@ -300,13 +300,14 @@ hipError_t launch_cfg_rs(const bf16* A, const bf16* W, int N, int K, int m_upper
 // workgroups per CU); a round costs about the same whatever the tile count in it, so the
 // estimate is rounds x the cost of one round of that tile relative to 128 x 128. Measured on
 // the 360M-shape projections: a round of 192 x 128 or 128 x 192 tiles (1.5x the work) costs
-// about 1.25 rounds of 128 x 128, the larger tiles reusing each LDS byte more. The 256-wide
-// tiles (one workgroup per CU) never won on these shapes and are left to MOR_GEMM_TILE.
+// about 1.25 rounds of 128 x 128, the larger tiles reusing each LDS byte more; on a tie the
+// taller activation tile (128 x 192) goes first, measured 1-3% faster than 192 x 128 there. The
+// 256-wide tiles (one workgroup per CU) never won on these shapes and are left to MOR_GEMM_TILE.
 struct TileCfg {
   int bn, bm, per_cu;
   double round_cost;
 };
-constexpr TileCfg kTiles[] = {{128, 128, 2, 1.0}, {192, 128, 2, 1.25}, {128, 192, 2, 1.25}};
+constexpr TileCfg kTiles[] = {{128, 128, 2, 1.0}, {128, 192, 2, 1.25}, {192, 128, 2, 1.25}};
 
 int choose_tile(int epi, int N, int m_upper) {
   int best = 0;
@@ -318,7 +319,7 @@ int choose_tile(int epi, int N, int m_upper) {
     const double t = (double)((tiles + slots - 1) / slots) * kTiles[c].round_cost;
     if (t < best_t - 1e-9) { best_t = t; best = c; }
   }
-  return best == 0 ? 3 : best == 1 ? 4 : 5;
+  return kTiles[best].bn == 192 ? 4 : kTiles[best].bm == 192 ? 5 : 3;
 }
 
 }  // namespace
