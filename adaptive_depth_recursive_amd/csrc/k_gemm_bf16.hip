@@ -257,8 +257,9 @@ int group_m() {
   return g_group_m;
 }
 
-// Tile override MOR_GEMM_TILE ("128x128", "192x128", "128x192", "256x128", "256x256"); read at
-// every launch (a getenv per projection), so a process can change it between calls.
+// Tile override MOR_GEMM_TILE ("128x128", "192x128", "128x192", "128x96", "128x64", "256x128",
+// "256x256"); read at every launch (a getenv per projection), so a process can change it
+// between calls.
 int forced_tile() {
   const char* s = getenv("MOR_GEMM_TILE");
   if (!s) return 0;
@@ -267,6 +268,8 @@ int forced_tile() {
   if (!strcmp(s, "128x128")) return 3;
   if (!strcmp(s, "192x128")) return 4;
   if (!strcmp(s, "128x192")) return 5;
+  if (!strcmp(s, "128x96")) return 6;
+  if (!strcmp(s, "128x64")) return 7;
   return 0;
 }
 
@@ -301,25 +304,29 @@ hipError_t launch_cfg_rs(const bf16* A, const bf16* W, int N, int K, int m_upper
 // estimate is rounds x the cost of one round of that tile relative to 128 x 128. Measured on
 // the 360M-shape projections: a round of 192 x 128 or 128 x 192 tiles (1.5x the work) costs
 // about 1.25 rounds of 128 x 128, the larger tiles reusing each LDS byte more; on a tie the
-// taller activation tile (128 x 192) goes first, measured 1-3% faster than 192 x 128 there. The
-// 256-wide tiles (one workgroup per CU) never won on these shapes and are left to MOR_GEMM_TILE.
+// taller activation tile (128 x 192) goes first, measured 1-3% faster than 192 x 128 there. A
+// round of 128 x 96 tiles costs about 0.92 of a 128 x 128 round: it wins where 128 x 128 leaves
+// a single round unevenly filled (the residual projections at a third of the tokens, 8% faster).
+// The 256-wide tiles (one workgroup per CU) and 128 x 64 never won on these shapes and are left
+// to MOR_GEMM_TILE.
 struct TileCfg {
   int bn, bm, per_cu;
   double round_cost;
 };
-constexpr TileCfg kTiles[] = {{128, 128, 2, 1.0}, {128, 192, 2, 1.25}, {192, 128, 2, 1.25}};
+constexpr TileCfg kTiles[] = {{128, 128, 2, 1.0}, {128, 192, 2, 1.25}, {192, 128, 2, 1.25}, {128, 96, 2, 0.92}};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 int choose_tile(int epi, int N, int m_upper) {
   int best = 0;
   double best_t = 1e300;
-  for (int c = 0; c < 3; ++c) {
+  for (int c = 0; c < kNumTiles; ++c) {
     if (kTiles[c].bn == 192 && epi == EPI_QKV) continue;   // the QKV epilogue needs 64-wide halves
     const long tiles = (long)((N + kTiles[c].bn - 1) / kTiles[c].bn) * ((m_upper + kTiles[c].bm - 1) / kTiles[c].bm);
     const long slots = 256L * kTiles[c].per_cu;
     const double t = (double)((tiles + slots - 1) / slots) * kTiles[c].round_cost;
     if (t < best_t - 1e-9) { best_t = t; best = c; }
   }
-  return kTiles[best].bn == 192 ? 4 : kTiles[best].bm == 192 ? 5 : 3;
+  return kTiles[best].bn == 192 ? 4 : kTiles[best].bm == 192 ? 5 : kTiles[best].bm == 96 ? 6 : 3;
 }
 
 }  // namespace
@@ -340,6 +347,8 @@ hipError_t launch_gemm<bf16>(int epi, const bf16* A, const bf16* W, int N, int K
       if (epi == EPI_RESID) return launch_cfg_rs<192, 128, EPI_RESID>(A, W, N, K, m_upper, meta, ep, s);
       return launch_cfg_rs<192, 128, EPI_SWIGLU>(A, W, N, K, m_upper, meta, ep, s);
     case 5: return launch_cfg<128, 192>(epi, A, W, N, K, m_upper, meta, ep, s);
+    case 6: return launch_cfg<128, 96>(epi, A, W, N, K, m_upper, meta, ep, s);
+    case 7: return launch_cfg<128, 64>(epi, A, W, N, K, m_upper, meta, ep, s);
     default: return launch_cfg<128, 128>(epi, A, W, N, K, m_upper, meta, ep, s);
   }
 }
