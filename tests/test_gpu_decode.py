@@ -137,6 +137,19 @@ def test_decode_wide_rows_f32_free_running():
     model.close()
 
 
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (8, 2)])
+def test_decode_bf16_gqa_ratios(hq, hkv):
+    """Decode attention with 1, 2 and 4 query heads per KV head, bf16 teacher-forced."""
+    cfg = workload.get_config("small_thr_bf16", n_q_heads=hq, n_kv_heads=hkv)
+    model, W, lens = _setup(cfg, slots=5)
+    inputs = workload.make_decode_inputs(cfg, lens)
+    res = _run(model, cfg, lens, inputs)
+    _check_routing(cfg, W, res, lens)
+    worst = _compare(cfg, W, res, lens, inputs, teacher=True)
+    say(f"[gpu] decode bf16 {hq}/{hkv} heads: worst rel err {worst:.2e}")
+    model.close()
+
+
 def test_decode_small_bf16_teacher_forced():
     cfg = workload.get_config("small_thr_bf16")
     model, W, lens = _setup(cfg, slots=5)

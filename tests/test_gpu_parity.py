@@ -78,6 +78,12 @@ def test_small_bf16_forced_gemm_tiles(tile, monkeypatch):
     _compare_prefill(workload.get_config("small_bf16"))
 
 
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (8, 2)])
+def test_small_bf16_gqa_ratios(hq, hkv):
+    """bf16 attention with 1, 2 and 4 query heads per KV head (the 360M shape has 3)."""
+    _compare_prefill(workload.get_config("small_bf16", n_q_heads=hq, n_kv_heads=hkv))
+
+
 def test_small_bf16_kv_share():
     _compare_prefill(workload.get_config("small_share_bf16"))
 
