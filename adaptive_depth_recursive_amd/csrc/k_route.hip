@@ -391,26 +391,34 @@ hipError_t launch_scatter(float* H, const float* X, int d, const int* meta, int 
 
 // ------------------------------------------------------------------ RMSNorm
 // One wave per row: Xn = X / sqrt(mean(X^2) + eps) * g, rounded to the GEMM input type.
+// m_upper bounds the row count meta[0] (rows below it are allocated): with CH > 0 the row and
+// the gains are loaded before the row count is known (row index clamped below m_upper), so the
+// kernel waits for one memory round trip, not three.
 template <typename T, int CH>
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ X, int d,
-                                                 const int* __restrict__ meta,
+                                                 const int* __restrict__ meta, int m_upper,
                                                  const float* __restrict__ g, float eps,
                                                  T* __restrict__ Xn) {
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = lane_id();
-  if (i >= meta[0]) return;
-  const float4* x = reinterpret_cast<const float4*>(X + (size_t)i * d);
   const float4* g4 = reinterpret_cast<const float4*>(g);
-  T* out = Xn + (size_t)i * d;
   const int n4 = d / 4;
   if constexpr (CH > 0) {
     // the row stays in registers (CH float4 per lane): one read of X
-    float4 v[CH];
+    const float4* x = reinterpret_cast<const float4*>(X + (size_t)min(i, m_upper - 1) * d);
+    float4 v[CH], gg[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int c = min(lane + k * WAVE, n4 - 1);
+      v[k] = x[c];
+      gg[k] = g4[c];
+    }
+    if (i >= meta[0]) return;
+    T* out = Xn + (size_t)i * d;
     float ss = 0.f;
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-      const int c = lane + k * WAVE;
-      v[k] = c < n4 ? x[c] : float4{0.f, 0.f, 0.f, 0.f};
+      if (lane + k * WAVE >= n4) v[k] = float4{0.f, 0.f, 0.f, 0.f};
       ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
     }
     ss = wave_sum(ss);
@@ -418,13 +426,14 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ X, in
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const int c = lane + k * WAVE;
-      if (c < n4) {
-        const float4 gg = g4[c];
-        Vec4<T>::store(out + 4 * c, v[k].x * rinv * gg.x, v[k].y * rinv * gg.y, v[k].z * rinv * gg.z,
-                       v[k].w * rinv * gg.w);
-      }
+      if (c < n4)
+        Vec4<T>::store(out + 4 * c, v[k].x * rinv * gg[k].x, v[k].y * rinv * gg[k].y,
+                       v[k].z * rinv * gg[k].z, v[k].w * rinv * gg[k].w);
     }
   } else {
+    if (i >= meta[0]) return;
+    const float4* x = reinterpret_cast<const float4*>(X + (size_t)i * d);
+    T* out = Xn + (size_t)i * d;
     float ss = 0.f;
     for (int c = lane; c < n4; c += WAVE) {
       const float4 v = x[c];
@@ -446,9 +455,9 @@ hipError_t launch_rmsnorm(const float* X, int d, const int* meta, int m_upper, c
   if (m_upper <= 0) return hipSuccess;
   const dim3 grid((m_upper + 3) / 4);
   if (d <= 4 * 4 * WAVE)
-    hipLaunchKernelGGL((k_rmsnorm<T, 4>), grid, dim3(256), 0, s, X, d, meta, g, eps, Xn);
+    hipLaunchKernelGGL((k_rmsnorm<T, 4>), grid, dim3(256), 0, s, X, d, meta, m_upper, g, eps, Xn);
   else
-    hipLaunchKernelGGL((k_rmsnorm<T, 0>), grid, dim3(256), 0, s, X, d, meta, g, eps, Xn);
+    hipLaunchKernelGGL((k_rmsnorm<T, 0>), grid, dim3(256), 0, s, X, d, meta, m_upper, g, eps, Xn);
   return hipGetLastError();
 }
 template hipError_t launch_rmsnorm<float>(const float*, int, const int*, int, const float*, float, float*, hipStream_t);
