@@ -1,6 +1,6 @@
 """GPU parity of the HIP library against the CPU oracle (needs an MI355X).
 
-Bars (BASELINE the benchmark spec): routing bit-exact (selected positions, counts, and the fp32 router
+Bars: routing bit-exact (selected positions, counts, and the fp32 router
 logits given the same H); hidden states within max relative error 1e-4 (fp32 configs) and
 2e-2 (bf16 configs), per token row as max|diff| / max|ref|.
 fp32 configs run free (the oracle makes its own routing decisions and must agree). bf16
