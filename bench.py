@@ -92,6 +92,31 @@ def traffic_from_profile(kernel: str, workload_name: str):
     return rec.get("bytes_per_launch")
 
 
+DECODE_SOURCES = ("adaptive_depth_recursive_amd/csrc/k_decode.hip",
+                  "adaptive_depth_recursive_amd/csrc/mor_api.hip")
+
+
+def decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in DECODE_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def decode_traffic_from_profile():
+    """HBM-side bytes per decode iteration from the committed counter summary, if it was taken
+    on the current decode kernels and launch sequence (null otherwise)."""
+    path = os.path.join(ROOT, "profiles", "decode_smol360m_mor4_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != decode_source_hash():
+        return None
+    return rec.get("bytes_per_iteration")
+
+
 def cpu_baseline(cfg, weights, H0_np, seq_len: int):
     """The oracle, as it stands, on one sequence of the same workload (host cores)."""
     import numpy as np
@@ -159,7 +184,8 @@ def decode_bench(args, kv_mode="recursion"):
         "window": f"{it} iterations ({chunks} chunks of {args.decode_chunk}) while the queue of "
                   f"{len(lens)} requests was not empty, after {args.decode_warmup} warmup iterations",
         "roofline": {"bound": "hbm", "achieved": byt / s_ / 1e9 if s_ else None, "peak": PEAK_HBM / 1e9,
-                     "unit": "GB/s", "frac": byt / s_ / PEAK_HBM if s_ else None, "traffic": None,
+                     "unit": "GB/s", "frac": byt / s_ / PEAK_HBM if s_ else None,
+                     "traffic": decode_traffic_from_profile() if kv_mode == "recursion" else None,
                      "algorithmic_bytes_per_iteration": byt / max(it, 1),
                      "kv_read_bytes_per_iteration": kvr / max(it, 1)},
         "exit_depth_histogram": np.bincount(done, minlength=cfg.n_rec + 1)[1:].tolist(),
