@@ -673,8 +673,8 @@ mor_status mor_init(const mor_config* cfg, const mor_weights* w, void* workspace
   if (e == hipSuccess && h->decode) {
     const int d = cfg->d_model;
     e = hipMemsetAsync(h->dXn, 0, 64 * (size_t)d * h->es, s);
-    if (e == hipSuccess) e = hipMemsetAsync(h->dQkv, 0, 4 * 64 * (size_t)h->nqkv * 4, s);
-    if (e == hipSuccess) e = hipMemsetAsync(h->dPx, 0, 8 * 64 * (size_t)d * 4, s);
+    if (e == hipSuccess) e = hipMemsetAsync(h->dQkv, 0, (size_t)kSplitQKV * 64 * h->nqkv * 4, s);
+    if (e == hipSuccess) e = hipMemsetAsync(h->dPx, 0, (size_t)kSplitPx * 64 * d * 4, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->dO, 0, 64 * (size_t)h->nq * h->es, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->dHf, 0, 64 * (size_t)cfg->d_ff * h->es, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->dec.glob, 0, G_COUNT * 4, s);
