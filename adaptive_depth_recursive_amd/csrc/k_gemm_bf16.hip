@@ -8,10 +8,10 @@
 //  - LDS rows are 128 bytes (64 bf16 of K) with the 16-byte chunks XOR-swizzled by
 //    (row >> 1) & 7, so the ds_read_b128 fragment reads of 16 consecutive rows hit 16 distinct
 //    bank groups;
-//  - 4 waves in 2 x 2, each owning a (BN/2) x (BM/2) block of the output (BN weight rows x BM
-//    activation rows per tile: 128 x 128, 192 x 128 or 128 x 192 at two workgroups per CU,
-//    256 x 128 and 256 x 256 at one); the tile is chosen per launch from the number of rounds
-//    of resident workgroups it needs (choose_tile below);
+//  - 2 x NWM waves (4 or 8), each owning a (BN/2) x (BM/NWM) block of the output (BN weight
+//    rows x BM activation rows per tile: four waves at 128 x 128, 192 x 128, 128 x 192 or 128 x 96
+//    with two workgroups per CU, eight waves at 256 x 256 with one); the tile is chosen per
+//    launch from the number of rounds of resident workgroups it needs (choose_tile below);
 //  - two LDS stages: the loads of step k+1 are in flight while step k is multiplied;
 //  - workgroups are renumbered so that the ones sharing an activation tile land on one XCD
 //    (the hardware deals workgroups round-robin over the 8 XCDs, each with its own L2).
@@ -30,14 +30,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// Issue one stage's loads of NI wave instructions for one operand: instruction i moves the 8
-// rows starting at (4 i + wave) * 8, each lane its 16-byte chunk at element offset off[i] from
-// `base`.
-template <int NI>
+// Issue one stage's loads of NI wave instructions for one operand: with NW waves, instruction i
+// moves the 8 rows starting at (NW i + wave) * 8, each lane its 16-byte chunk at element offset
+// off[i] from `base`.
+template <int NI, int NW>
 __device__ __forceinline__ void load_stage(const bf16* base, const int* off, char* dst, int wave) {
 #pragma unroll
   for (int i = 0; i < NI; ++i)
-    __builtin_amdgcn_global_load_lds(base + off[i], (lds_void*)(dst + (i * 4 + wave) * 8 * kRowBytes), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(base + off[i], (lds_void*)(dst + (i * NW + wave) * 8 * kRowBytes), 16, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 frag(const char* base, int row, int chunk) {
@@ -46,12 +46,12 @@ __device__ __forceinline__ bf16x8 frag(const char* base, int row, int chunk) {
 
 }  // namespace
 
-template <int BN, int BM, int EPI>
-__global__ __launch_bounds__(256, 1) void k_gemm_bf16(const bf16* __restrict__ A,
+template <int BN, int BM, int EPI, int NWM = 2>
+__global__ __launch_bounds__(128 * NWM, 1) void k_gemm_bf16(const bf16* __restrict__ A,
                                                       const bf16* __restrict__ W, int N, int K,
                                                       int tiles_n, int group_m,
                                                       const int* __restrict__ meta, GemmEpi ep) {
-  constexpr int WN = BN / 2, WM = BM / 2;
+  constexpr int WN = BN / 2, WM = BM / NWM;
   constexpr int FN = WN / 16, FM = WM / 16;
   constexpr int STAGE = (BN + BM) * kRowBytes;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(const bf16* __restrict__ A
   if (m0 >= M) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave >> 1, wm = wave & 1;
+  const int wn = wave / NWM, wm = wave % NWM;
   const int fr = lane & 15, g = lane >> 4;
 
   f32x4 acc[FN][FM];
@@ -89,24 +89,26 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(const bf16* __restrict__ A
   // 1 KB = 8 rows x 128 bytes, contiguous in LDS; lane l loads the global 16-byte chunk that
   // lands at slot l & 7 of its row. The per-lane element offsets (from the tile's first row,
   // rows clamped into the operand) are computed once; a stage only adds its K offset.
-  constexpr int IW = BN / 32, IA = BM / 32;       // load instructions per wave per stage
+  constexpr int NW = 2 * NWM;                     // waves: 2 along the weight rows x NWM
+  constexpr int IW = BN / (8 * NW), IA = BM / (8 * NW);   // load instructions per wave per stage
+  static_assert(IW * 8 * NW == BN && IA * 8 * NW == BM, "tile rows must split over the waves");
   const bf16* Wt = W + (size_t)n0 * K;
   const bf16* At = A + (size_t)m0 * K;
   int offw[IW], offa[IA];
 #pragma unroll
   for (int i = 0; i < IW; ++i) {
-    const int r = (i * 4 + wave) * 8 + (lane >> 3);
+    const int r = (i * NW + wave) * 8 + (lane >> 3);
     offw[i] = min(r, N - 1 - n0) * K + ((lane & 7) ^ swz(r)) * 8;
   }
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
-    const int r = (i * 4 + wave) * 8 + (lane >> 3);
+    const int r = (i * NW + wave) * 8 + (lane >> 3);
     offa[i] = min(r, M - 1 - m0) * K + ((lane & 7) ^ swz(r)) * 8;
   }
   auto issue = [&](int kt, int buf) {
     char* st = smem + buf * STAGE;
-    load_stage<IW>(Wt + kt * 64, offw, st, wave);
-    load_stage<IA>(At + kt * 64, offa, st + BN * kRowBytes, wave);
+    load_stage<IW, NW>(Wt + kt * 64, offw, st, wave);
+    load_stage<IA, NW>(At + kt * 64, offa, st + BN * kRowBytes, wave);
   };
 
   const int g4 = g * 4;
@@ -258,8 +260,8 @@ int group_m() {
 }
 
 // Tile override MOR_GEMM_TILE ("128x128", "192x128", "128x192", "128x96", "128x64", "256x128",
-// "256x256"); read at every launch (a getenv per projection), so a process can change it
-// between calls.
+// "256x256", and the eight-wave "256x192w8", "192x256w8", "256x256w8"); read at every launch (a
+// getenv per projection), so a process can change it between calls.
 int forced_tile() {
   const char* s = getenv("MOR_GEMM_TILE");
   if (!s) return 0;
@@ -270,6 +272,9 @@ int forced_tile() {
   if (!strcmp(s, "128x192")) return 5;
   if (!strcmp(s, "128x96")) return 6;
   if (!strcmp(s, "128x64")) return 7;
+  if (!strcmp(s, "256x192w8")) return 8;
+  if (!strcmp(s, "192x256w8")) return 9;
+  if (!strcmp(s, "256x256w8")) return 10;
   return 0;
 }
 
@@ -299,6 +304,22 @@ hipError_t launch_cfg_rs(const bf16* A, const bf16* W, int N, int K, int m_upper
   return hipGetLastError();
 }
 
+// Eight waves (2 x 4) per workgroup, one workgroup per CU.
+template <int BN, int BM>
+hipError_t launch_cfg8(int epi, const bf16* A, const bf16* W, int N, int K, int m_upper,
+                       const int* meta, const GemmEpi& ep, hipStream_t s) {
+  const int tn = (N + BN - 1) / BN, tm = (m_upper + BM - 1) / BM;
+  const int nblk = tn * tm;
+  if (nblk == 0) return hipSuccess;
+  const int gm = group_m();
+  switch (epi) {
+    case EPI_QKV: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_QKV, 4>), dim3(nblk), dim3(512), 0, s, A, W, N, K, tn, gm, meta, ep); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_RESID, 4>), dim3(nblk), dim3(512), 0, s, A, W, N, K, tn, gm, meta, ep); break;
+    default: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_SWIGLU, 4>), dim3(nblk), dim3(512), 0, s, A, W, N, K, tn, gm, meta, ep); break;
+  }
+  return hipGetLastError();
+}
+
 // Tile choice. A launch runs in rounds of as many tiles as fit on the chip at once (256 CUs x
 // workgroups per CU); a round costs about the same whatever the tile count in it, so the
 // estimate is rounds x the cost of one round of that tile relative to 128 x 128. Measured on
@@ -307,13 +328,17 @@ hipError_t launch_cfg_rs(const bf16* A, const bf16* W, int N, int K, int m_upper
 // taller activation tile (128 x 192) goes first, measured 1-3% faster than 192 x 128 there. A
 // round of 128 x 96 tiles costs about 0.92 of a 128 x 128 round: it wins where 128 x 128 leaves
 // a single round unevenly filled (the residual projections at a third of the tokens, 8% faster).
-// The 256-wide tiles (one workgroup per CU) and 128 x 64 never won on these shapes and are left
-// to MOR_GEMM_TILE.
+// A 256 x 256 tile of eight waves (one workgroup per CU) costs about 1.9 rounds of 128 x 128: it
+// wins where 128 x 128 needs exactly two rounds (the residual projections at all 16,384 tokens,
+// 77.3 -> 73.8 us). The four-wave 256-wide tiles, 128 x 64 and the other eight-wave shapes
+// never won on these shapes and are left to MOR_GEMM_TILE.
 struct TileCfg {
   int bn, bm, per_cu;
   double round_cost;
+  int choice;       // forced_tile() value of the same tile
 };
-constexpr TileCfg kTiles[] = {{128, 128, 2, 1.0}, {128, 192, 2, 1.25}, {192, 128, 2, 1.25}, {128, 96, 2, 0.92}};
+constexpr TileCfg kTiles[] = {{128, 128, 2, 1.0, 3}, {128, 192, 2, 1.25, 5}, {192, 128, 2, 1.25, 4},
+                              {128, 96, 2, 0.92, 6}, {256, 256, 1, 1.9, 10}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 int choose_tile(int epi, int N, int m_upper) {
@@ -326,7 +351,7 @@ int choose_tile(int epi, int N, int m_upper) {
     const double t = (double)((tiles + slots - 1) / slots) * kTiles[c].round_cost;
     if (t < best_t - 1e-9) { best_t = t; best = c; }
   }
-  return kTiles[best].bn == 192 ? 4 : kTiles[best].bm == 192 ? 5 : kTiles[best].bm == 96 ? 6 : 3;
+  return kTiles[best].choice;
 }
 
 }  // namespace
@@ -349,6 +374,11 @@ hipError_t launch_gemm<bf16>(int epi, const bf16* A, const bf16* W, int N, int K
     case 5: return launch_cfg<128, 192>(epi, A, W, N, K, m_upper, meta, ep, s);
     case 6: return launch_cfg<128, 96>(epi, A, W, N, K, m_upper, meta, ep, s);
     case 7: return launch_cfg<128, 64>(epi, A, W, N, K, m_upper, meta, ep, s);
+    case 8: return launch_cfg8<256, 192>(epi, A, W, N, K, m_upper, meta, ep, s);
+    case 9:
+      if (epi == EPI_QKV) return launch_cfg8<256, 192>(epi, A, W, N, K, m_upper, meta, ep, s);
+      return launch_cfg8<192, 256>(epi, A, W, N, K, m_upper, meta, ep, s);
+    case 10: return launch_cfg8<256, 256>(epi, A, W, N, K, m_upper, meta, ep, s);
     default: return launch_cfg<128, 128>(epi, A, W, N, K, m_upper, meta, ep, s);
   }
 }
