@@ -70,7 +70,7 @@ def test_small_bf16_teacher_forced():
     _compare_prefill(workload.get_config("small_bf16"))
 
 
-@pytest.mark.parametrize("tile", ["128x128", "192x128", "128x192", "128x96", "128x64", "256x128", "256x256", "256x192w8", "192x256w8", "256x256w8"])
+@pytest.mark.parametrize("tile", ["128x128", "192x128", "128x192", "128x96", "128x64", "256x128", "256x256", "256x192w8", "192x256w8", "256x256w8", "128x192w8", "128x128w8"])
 def test_small_bf16_forced_gemm_tiles(tile, monkeypatch):
     """Every bf16 projection tile shape (forced for all projections; 192x128 falls back to
     128x128 for the QKV projection), with ragged row and column tails."""
