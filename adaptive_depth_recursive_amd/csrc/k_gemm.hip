@@ -104,6 +104,7 @@ __global__ __launch_bounds__(256) void k_gemm(const T* __restrict__ A, const T* 
   const int mw = m0 + wm * WM + fr;         // this lane's token row for frag j: mw + 16 j
 
   if constexpr (EPI == EPI_RESID) {
+    const float* xs = ep.xin ? ep.xin : ep.x;
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int m = mw + 16 * j;
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256) void k_gemm(const T* __restrict__ A, const T* 
         const int n = nw + 16 * i + g4;
         if (n >= N) continue;
         float4* px = reinterpret_cast<float4*>(ep.x + (size_t)m * ep.ldx + n);
-        float4 v = *px;
+        float4 v = *reinterpret_cast<const float4*>(xs + (size_t)m * ep.ldx + n);
         v.x += acc[i][j][0]; v.y += acc[i][j][1]; v.z += acc[i][j][2]; v.w += acc[i][j][3];
         *px = v;
       }

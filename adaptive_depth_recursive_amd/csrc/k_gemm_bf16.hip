@@ -133,7 +133,7 @@ __global__ __launch_bounds__(128 * NWM, (NWM == 4 && BN * BM <= 128 * 192) ? 2 :
 #pragma unroll
           for (int i = 0; i < FN; ++i) {
             const int m = mw + 16 * j, n = nw + 16 * i + g4;
-            xr[i][j] = (m < M && n < N) ? *reinterpret_cast<const float4*>(ep.x + (size_t)m * ep.ldx + n)
+            xr[i][j] = (m < M && n < N) ? *reinterpret_cast<const float4*>((ep.xin ? ep.xin : ep.x) + (size_t)m * ep.ldx + n)
                                         : float4{0.f, 0.f, 0.f, 0.f};
           }
       }
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(128 * NWM, (NWM == 4 && BN * BM <= 128 * 192) ? 2 :
         if (n >= N) continue;
         float4 v;
         if constexpr (kPrefetchX) v = xr[i][j];
-        else v = *reinterpret_cast<const float4*>(ep.x + (size_t)m * ep.ldx + n);
+        else v = *reinterpret_cast<const float4*>((ep.xin ? ep.xin : ep.x) + (size_t)m * ep.ldx + n);
         v.x += acc[i][j][0]; v.y += acc[i][j][1]; v.z += acc[i][j][2]; v.w += acc[i][j][3];
         *reinterpret_cast<float4*>(ep.x + (size_t)m * ep.ldx + n) = v;
       }

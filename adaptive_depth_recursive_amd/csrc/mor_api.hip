@@ -350,13 +350,16 @@ struct TimedLaunch {
   }
 };
 
+// One Llama block on the rows of rs, updating X in place; with x_in, the block's input rows are
+// read from x_in instead and X receives the output (every row of rs is written).
 template <typename E>
 mor_status run_layer(mor_handle_s* h, const BlockPacked& w, float* X, const RowSet& rs,
-                     void* k_dst, void* vt_dst, const KeySet& keys, int B, int T, hipStream_t s) {
+                     void* k_dst, void* vt_dst, const KeySet& keys, int B, int T, hipStream_t s,
+                     const float* x_in = nullptr) {
   const mor_config& c = h->cfg;
   const int d = c.d_model, dff = c.d_ff, MT = (int)h->MT;
   E* Xn = reinterpret_cast<E*>(h->Xn);
-  HIPCHK(launch_rmsnorm<E>(X, d, rs.meta, rs.m_upper, w.g_attn, c.rms_eps, Xn, s));
+  HIPCHK(launch_rmsnorm<E>(x_in ? x_in : X, d, rs.meta, rs.m_upper, w.g_attn, c.rms_eps, Xn, s));
 
   GemmEpi ep{};
   ep.q = h->Q; ep.ldq = h->nq;
@@ -383,10 +386,12 @@ mor_status run_layer(mor_handle_s* h, const BlockPacked& w, float* X, const RowS
 
   GemmEpi er{};
   er.x = X; er.ldx = d;
+  er.xin = x_in;
   {
     TimedLaunch t(h, KIND_O, s);
     HIPCHK(launch_gemm<E>(EPI_RESID, reinterpret_cast<const E*>(h->O), reinterpret_cast<const E*>(w.wo), d, h->nq, rs.m_upper, rs.meta, er, s));
   }
+  er.xin = nullptr;
   HIPCHK(launch_rmsnorm<E>(X, d, rs.meta, rs.m_upper, w.g_ffn, c.rms_eps, Xn, s));
   GemmEpi eg{};
   eg.h = h->Hf; eg.ldh = dff;
@@ -415,7 +420,10 @@ mor_status prefill_impl(mor_handle_s* h, const float* h_in, int B, int T, float*
   int ks[MOR_MAX_REC];
   for (int r = 0; r < R; ++r) ks[r] = ceil_div((long)c.cap_num[r] * T, c.cap_den);
 
-  if (H != h_in) HIPCHK(hipMemcpyAsync(H, h_in, hbytes, hipMemcpyDeviceToDevice, s));
+  const bool middle = middle_sharing(c);
+  // with a unique first layer the input enters the stream through that layer (it reads h_in and
+  // writes H); otherwise routing starts on a copy of the input
+  if (H != h_in && !middle) HIPCHK(hipMemcpyAsync(H, h_in, hbytes, hipMemcpyDeviceToDevice, s));
   int* meta_r[MOR_MAX_REC + 2];
   for (int r = 0; r <= R + 1; ++r) meta_r[r] = h->meta + (size_t)r * (c.max_batch + 1);
   auto act_r = [&](int r) { return h->act + (size_t)r * MT; };
@@ -427,11 +435,11 @@ mor_status prefill_impl(mor_handle_s* h, const float* h_in, int B, int T, float*
     HIPCHK(launch_fill_f32(h->z + MT, R * MT, NAN, s));
 
   const RowSet all{meta_r[0], cnt_r(0), h->rows_all, (int)BT, T};
-  const bool middle = middle_sharing(c);
   mor_status st = MOR_OK;
   if (middle) {
     const KeySet keys_first{kv_k(h, 0), kv_vt(h, 0), act_r(0), cnt_r(0)};
-    st = run_layer<E>(h, h->blk[0], H, all, kv_k(h, 0), kv_vt(h, 0), keys_first, B, T, s);
+    st = run_layer<E>(h, h->blk[0], H, all, kv_k(h, 0), kv_vt(h, 0), keys_first, B, T, s,
+                      H != h_in ? h_in : nullptr);
     if (st != MOR_OK) return st;
   }
   if (h_per_rec) HIPCHK(hipMemcpyAsync(h_per_rec, H, hbytes, hipMemcpyDeviceToDevice, s));

@@ -19,8 +19,9 @@ struct GemmEpi {
   const int* rowidx;                // index of the row inside its sequence's active list
   const float* rope_cos;            // [max_seq][hd/2]
   const float* rope_sin;
-  // EPI_RESID
+  // EPI_RESID: x[m][n] = xin[m][n] + acc (xin == nullptr: x is read and written in place)
   float* x; int ldx;
+  const float* xin;
   // EPI_SWIGLU
   void* h; int ldh;
 };
