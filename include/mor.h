@@ -142,7 +142,10 @@ mor_status mor_init(const mor_config* cfg, const mor_weights* w, void* workspace
 /* MoR prefill of B sequences of T tokens (MoR paper A.1-A.3; reading notes 1, 2, 3).
  *   h_in   device fp32 [B][T][d]   input hidden states H^0.
  *   h_out  device fp32 [B][T][d]   output H^L after the last layer (no final norm, no LM head).
- *                                  May equal h_in. Also serves as the fp32 residual stream.
+ *                                  May equal h_in (then h_in is overwritten); must not
+ *                                  otherwise overlap it. Also serves as the fp32 residual
+ *                                  stream. With a unique first layer, h_in is only read by that
+ *                                  layer (no copy of it is made).
  * Optional outputs (NULL to skip), all device memory:
  *   sel_pos   int32 [N_r][B][T]  positions of the tokens active at recursion r, ascending, -1 padded.
  *   counts    int32 [N_r][B]     number of active tokens per recursion and sequence.
