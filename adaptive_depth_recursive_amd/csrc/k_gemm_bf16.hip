@@ -14,8 +14,10 @@
 //    tile is chosen per launch from the number of rounds of resident workgroups it needs
 //    (choose_tile below);
 //  - two LDS stages: the loads of step k+1 are in flight while step k is multiplied;
-//  - workgroups are renumbered so that the ones sharing an activation tile land on one XCD
-//    (the hardware deals workgroups round-robin over the 8 XCDs, each with its own L2).
+//  - persistent workgroups (no more than are resident at once), each XCD owning a contiguous
+//    range of the tile order so that the workgroups sharing an activation tile share its L2
+//    (the hardware deals workgroups round-robin over the 8 XCDs); a workgroup issues its next
+//    tile's first stage before the current tile's epilogue.
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
@@ -50,7 +52,7 @@ __device__ __forceinline__ bf16x8 frag(const char* base, int row, int chunk) {
 template <int BN, int BM, int EPI, int NWM = 2>
 __global__ __launch_bounds__(128 * NWM, (NWM == 4 && BN * BM <= 128 * 192) ? 2 : 1) void k_gemm_bf16(const bf16* __restrict__ A,
                                                       const bf16* __restrict__ W, int N, int K,
-                                                      int tiles_n, int group_m,
+                                                      int tiles_n, int ntiles, int group_m,
                                                       const int* __restrict__ meta, GemmEpi ep) {
   constexpr int WN = BN / 2, WM = BM / NWM;
   constexpr int FN = WN / 16, FM = WM / 16;
@@ -58,33 +60,43 @@ __global__ __launch_bounds__(128 * NWM, (NWM == 4 && BN * BM <= 128 * 192) ? 2 :
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int M = meta[0];
-  // XCD-aware renumbering: blocks b, b+8, b+16, ... run on one XCD; give them consecutive
-  // positions of the tile order.
-  const int nblk = gridDim.x;
-  const int bid = blockIdx.x;
-  const int per_xcd = nblk / 8, rem = nblk % 8;
+  // Persistent workgroups: the grid holds at most as many workgroups as are resident at once,
+  // and each takes a sequence of tiles. The hardware deals workgroups round-robin over the 8
+  // XCDs (each with its own L2), so XCD x owns one contiguous range of the tile order and its
+  // workgroups take that range's tiles in turn (round k of an XCD covers consecutive tiles).
+  const int G = gridDim.x, bid = blockIdx.x;
   const int xcd = bid % 8, slot = bid / 8;
-  const int t = (xcd < rem ? xcd * (per_xcd + 1) : rem * (per_xcd + 1) + (xcd - rem) * per_xcd) + slot;
+  const int wpx = G / 8 + (xcd < G % 8 ? 1 : 0);            // workgroups on this XCD
+  const int tpx = ntiles / 8, trem = ntiles % 8;
+  const int tbase = xcd < trem ? xcd * (tpx + 1) : trem * (tpx + 1) + (xcd - trem) * tpx;
+  const int tend = tbase + tpx + (xcd < trem ? 1 : 0);
   // Tile order: groups of group_m activation row-blocks, swept one weight column-block at a
   // time with the row-blocks fastest, so the workgroups resident on an XCD share a few
   // activation slabs and a few weight slabs in its L2.
-  const int tiles_m = nblk / tiles_n;
+  const int tiles_m = ntiles / tiles_n;
   const int gsz = group_m * tiles_n;
-  const int grp = t / gsz, gi = t - grp * gsz;
-  const int rows_g = min(group_m, tiles_m - grp * group_m);
-  const int tm = grp * group_m + gi % rows_g, tn = gi / rows_g;
-  const int m0 = tm * BM, n0 = tn * BN;
-  if (m0 >= M) return;
+  // the next tile of this workgroup at or after position t that has rows (m0 < M); -1 if none
+  auto next_tile = [&](int t, int& m0, int& n0) -> int {
+    for (; t < tend; t += wpx) {
+      const int grp = t / gsz, gi = t - grp * gsz;
+      const int rows_g = min(group_m, tiles_m - grp * group_m);
+      const int tm = grp * group_m + gi % rows_g, tn = gi / rows_g;
+      if (tm * BM < M) {
+        m0 = tm * BM; n0 = tn * BN;
+        return t;
+      }
+    }
+    return -1;
+  };
+  int m0 = 0, n0 = 0;
+  int t = next_tile(tbase + slot, m0, n0);
+  if (t < 0) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave / NWM, wm = wave % NWM;
   const int fr = lane & 15, g = lane >> 4;
 
   f32x4 acc[FN][FM];
-#pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Operand tiles move global -> LDS with global_load_lds_dwordx4: one wave instruction writes
   // 1 KB = 8 rows x 128 bytes, contiguous in LDS; lane l loads the global 16-byte chunk that
@@ -93,164 +105,198 @@ __global__ __launch_bounds__(128 * NWM, (NWM == 4 && BN * BM <= 128 * 192) ? 2 :
   constexpr int NW = 2 * NWM;                     // waves: 2 along the weight rows x NWM
   constexpr int IW = BN / (8 * NW), IA = BM / (8 * NW);   // load instructions per wave per stage
   static_assert(IW * 8 * NW == BN && IA * 8 * NW == BM, "tile rows must split over the waves");
-  const bf16* Wt = W + (size_t)n0 * K;
-  const bf16* At = A + (size_t)m0 * K;
+  const bf16* Wt;
+  const bf16* At;
   int offw[IW], offa[IA];
+  auto setup = [&](int tm0, int tn0) {
+    Wt = W + (size_t)tn0 * K;
+    At = A + (size_t)tm0 * K;
 #pragma unroll
-  for (int i = 0; i < IW; ++i) {
-    const int r = (i * NW + wave) * 8 + (lane >> 3);
-    offw[i] = min(r, N - 1 - n0) * K + ((lane & 7) ^ swz(r)) * 8;
-  }
+    for (int i = 0; i < IW; ++i) {
+      const int r = (i * NW + wave) * 8 + (lane >> 3);
+      offw[i] = min(r, N - 1 - tn0) * K + ((lane & 7) ^ swz(r)) * 8;
+    }
 #pragma unroll
-  for (int i = 0; i < IA; ++i) {
-    const int r = (i * NW + wave) * 8 + (lane >> 3);
-    offa[i] = min(r, M - 1 - m0) * K + ((lane & 7) ^ swz(r)) * 8;
-  }
+    for (int i = 0; i < IA; ++i) {
+      const int r = (i * NW + wave) * 8 + (lane >> 3);
+      offa[i] = min(r, M - 1 - tm0) * K + ((lane & 7) ^ swz(r)) * 8;
+    }
+  };
   auto issue = [&](int kt, int buf) {
     char* st = smem + buf * STAGE;
     load_stage<IW, NW>(Wt + kt * 64, offw, st, wave);
     load_stage<IA, NW>(At + kt * 64, offa, st + BN * kRowBytes, wave);
   };
 
-  const int g4 = g * 4;
-  const int nw = n0 + wn * WN;
-  const int mw = m0 + wm * WM + fr;
-  // residual epilogue of the 128 x 128 tile: the stream values this lane updates are loaded
-  // during the last stage's matrix ops (no stage loads are in flight then), not after them
-  constexpr bool kPrefetchX = EPI == EPI_RESID && BN * BM <= 128 * 128;
-  float4 xr[kPrefetchX ? FN : 1][kPrefetchX ? FM : 1];
-
   const int nk = K / 64;
+  setup(m0, n0);
   issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
-    if constexpr (kPrefetchX) {
-      if (kt + 1 == nk) {
+  int buf0 = 0;                                   // LDS stage of this tile's first K step
+  for (;;) {
+    const int g4 = g * 4;
+    const int nw = n0 + wn * WN;
+    const int mw = m0 + wm * WM + fr;
 #pragma unroll
-        for (int j = 0; j < FM; ++j)
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-          for (int i = 0; i < FN; ++i) {
-            const int m = mw + 16 * j, n = nw + 16 * i + g4;
-            xr[i][j] = (m < M && n < N) ? *reinterpret_cast<const float4*>((ep.xin ? ep.xin : ep.x) + (size_t)m * ep.ldx + n)
-                                        : float4{0.f, 0.f, 0.f, 0.f};
-          }
-      }
-    }
-    const char* sw = smem + (kt & 1) * STAGE;
-    const char* sa = sw + BN * kRowBytes;
-    // both 32-deep halves' fragments are requested up front: the second half's reads are in
-    // flight while the first half multiplies
-    bf16x8 a[2][FN], b[2][FM];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int i = 0; i < FN; ++i) a[ks][i] = frag(sw, wn * WN + i * 16 + fr, ks * 4 + g);
-#pragma unroll
-      for (int j = 0; j < FM; ++j) b[ks][j] = frag(sa, wm * WM + j * 16 + fr, ks * 4 + g);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
-    // keep that order through scheduling: the first half's reads, then its matrix ops with the
-    // second half's reads spread between them, then the second half's matrix ops
-    __builtin_amdgcn_sched_group_barrier(0x100, FN + FM, 0);
-#pragma unroll
-    for (int r = 0; r < FN + FM; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, FN * FM / (FN + FM), 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, FN * FM, 0);
-  }
+      for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // residual epilogue of the 128 x 128 tile: the stream values this lane updates are loaded
+    // during the last stage's matrix ops (no stage loads are in flight then), not after them
+    constexpr bool kPrefetchX = EPI == EPI_RESID && BN * BM <= 128 * 128;
+    float4 xr[kPrefetchX ? FN : 1][kPrefetchX ? FM : 1];
 
-  // ------------------------------------------------------------------ epilogues
-  if constexpr (EPI == EPI_RESID) {
+    for (int kt = 0; kt < nk; ++kt) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kt + 1 < nk) issue(kt + 1, (buf0 + kt + 1) & 1);
+      if constexpr (kPrefetchX) {
+        if (kt + 1 == nk) {
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int m = mw + 16 * j;
-      if (m >= M) continue;
+          for (int j = 0; j < FM; ++j)
 #pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const int n = nw + 16 * i + g4;
-        if (n >= N) continue;
-        float4 v;
-        if constexpr (kPrefetchX) v = xr[i][j];
-        else v = *reinterpret_cast<const float4*>((ep.xin ? ep.xin : ep.x) + (size_t)m * ep.ldx + n);
-        v.x += acc[i][j][0]; v.y += acc[i][j][1]; v.z += acc[i][j][2]; v.w += acc[i][j][3];
-        *reinterpret_cast<float4*>(ep.x + (size_t)m * ep.ldx + n) = v;
-      }
-    }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int m = mw + 16 * j;
-      if (m >= M) continue;
-#pragma unroll
-      for (int i = 0; i < FN; i += 2) {
-        const int np = nw + 16 * i;
-        if (np >= N) continue;
-        float o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float gt = acc[i][j][e], up = acc[i + 1][j][e];
-          o[e] = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
+            for (int i = 0; i < FN; ++i) {
+              const int m = mw + 16 * j, n = nw + 16 * i + g4;
+              xr[i][j] = (m < M && n < N) ? *reinterpret_cast<const float4*>((ep.xin ? ep.xin : ep.x) + (size_t)m * ep.ldx + n)
+                                          : float4{0.f, 0.f, 0.f, 0.f};
+            }
         }
-        Vec4<bf16>::store(reinterpret_cast<bf16*>(ep.h) + (size_t)m * ep.ldh + (np >> 1) + g4,
-                          o[0], o[1], o[2], o[3]);
       }
+      const char* sw = smem + ((buf0 + kt) & 1) * STAGE;
+      const char* sa = sw + BN * kRowBytes;
+      // both 32-deep halves' fragments are requested up front: the second half's reads are in
+      // flight while the first half multiplies
+      bf16x8 a[2][FN], b[2][FM];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i) a[ks][i] = frag(sw, wn * WN + i * 16 + fr, ks * 4 + g);
+#pragma unroll
+        for (int j = 0; j < FM; ++j) b[ks][j] = frag(sa, wm * WM + j * 16 + fr, ks * 4 + g);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+          for (int j = 0; j < FM; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
+      // keep that order through scheduling: the first half's reads, then its matrix ops with the
+      // second half's reads spread between them, then the second half's matrix ops
+      __builtin_amdgcn_sched_group_barrier(0x100, FN + FM, 0);
+#pragma unroll
+      for (int r = 0; r < FN + FM; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, FN * FM / (FN + FM), 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, FN * FM, 0);
     }
-  } else {  // EPI_QKV, head_dim 64: the rotate-half partner of frag i is frag i + 2
+
+    // The next tile's first stage goes out before this tile's epilogue, into the stage the last
+    // K step did not read (every wave passed the barrier after its last reads of it), so its
+    // load latency overlaps the epilogue.
+    int nm0 = 0, nn0 = 0;
+    const int tnext = next_tile(t + wpx, nm0, nn0);
+    if (tnext >= 0) {
+      setup(nm0, nn0);
+      issue(0, (buf0 + nk) & 1);
+    }
+
+    // ------------------------------------------------------------------ epilogues
+    if constexpr (EPI == EPI_RESID) {
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int m = mw + 16 * j;
-      if (m >= M) continue;
-      const int pos = ep.rowpos[m];
-      const int bseq = ep.rowseq[m], bidx = ep.rowidx[m];
+      for (int j = 0; j < FM; ++j) {
+        const int m = mw + 16 * j;
+        if (m >= M) continue;
 #pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const int nf = nw + 16 * i;
-        if (nf >= N) continue;
-        if (nf < ep.nq + ep.nkv) {
-          if ((i & 3) >= 2) continue;               // second half: written with its partner
-          const int rbase = nf < ep.nq ? 0 : ep.nq;
-          const int c0 = (nf - rbase) & 63;         // 0 or 16
-          float lo[4], hi[4];
+        for (int i = 0; i < FN; ++i) {
+          const int n = nw + 16 * i + g4;
+          if (n >= N) continue;
+          float4 v;
+          if constexpr (kPrefetchX) v = xr[i][j];
+          else v = *reinterpret_cast<const float4*>((ep.xin ? ep.xin : ep.x) + (size_t)m * ep.ldx + n);
+          v.x += acc[i][j][0]; v.y += acc[i][j][1]; v.z += acc[i][j][2]; v.w += acc[i][j][3];
+          *reinterpret_cast<float4*>(ep.x + (size_t)m * ep.ldx + n) = v;
+        }
+      }
+    } else if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int m = mw + 16 * j;
+        if (m >= M) continue;
+#pragma unroll
+        for (int i = 0; i < FN; i += 2) {
+          const int np = nw + 16 * i;
+          if (np >= N) continue;
+          float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int f = c0 + g4 + e;
-            const float cs = ep.rope_cos[pos * 32 + f], sn = ep.rope_sin[pos * 32 + f];
-            const float x1 = acc[i][j][e], x2 = acc[i + 2][j][e];
-            lo[e] = x1 * cs - x2 * sn;
-            hi[e] = x2 * cs + x1 * sn;
+            const float gt = acc[i][j][e], up = acc[i + 1][j][e];
+            o[e] = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
           }
-          bf16* dst;
-          if (nf < ep.nq) {
-            dst = reinterpret_cast<bf16*>(ep.q) + (size_t)m * ep.ldq + nf + g4;
-          } else {
-            dst = reinterpret_cast<bf16*>(ep.k) + ((size_t)bseq * ep.kpad + bidx) * ep.nkv + (nf - ep.nq) + g4;
-          }
-          Vec4<bf16>::store(dst, lo[0], lo[1], lo[2], lo[3]);
-          Vec4<bf16>::store(dst + 32, hi[0], hi[1], hi[2], hi[3]);
-        } else {
-          const int vn = nf - ep.nq - ep.nkv + g4;
-          const int kvh = vn >> 6, dc = vn & 63;
-          bf16* vp = reinterpret_cast<bf16*>(ep.vt) + (((size_t)bseq * ep.hkv + kvh) * 64 + dc) * ep.kpad + bidx;
+          Vec4<bf16>::store(reinterpret_cast<bf16*>(ep.h) + (size_t)m * ep.ldh + (np >> 1) + g4,
+                            o[0], o[1], o[2], o[3]);
+        }
+      }
+    } else {  // EPI_QKV, head_dim 64: the rotate-half partner of frag i is frag i + 2
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vp[(size_t)e * ep.kpad] = (bf16)acc[i][j][e];
+      for (int j = 0; j < FM; ++j) {
+        const int m = mw + 16 * j;
+        if (m >= M) continue;
+        const int pos = ep.rowpos[m];
+        const int bseq = ep.rowseq[m], bidx = ep.rowidx[m];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          const int nf = nw + 16 * i;
+          if (nf >= N) continue;
+          if (nf < ep.nq + ep.nkv) {
+            if ((i & 3) >= 2) continue;               // second half: written with its partner
+            const int rbase = nf < ep.nq ? 0 : ep.nq;
+            const int c0 = (nf - rbase) & 63;         // 0 or 16
+            float lo[4], hi[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int f = c0 + g4 + e;
+              const float cs = ep.rope_cos[pos * 32 + f], sn = ep.rope_sin[pos * 32 + f];
+              const float x1 = acc[i][j][e], x2 = acc[i + 2][j][e];
+              lo[e] = x1 * cs - x2 * sn;
+              hi[e] = x2 * cs + x1 * sn;
+            }
+            bf16* dst;
+            if (nf < ep.nq) {
+              dst = reinterpret_cast<bf16*>(ep.q) + (size_t)m * ep.ldq + nf + g4;
+            } else {
+              dst = reinterpret_cast<bf16*>(ep.k) + ((size_t)bseq * ep.kpad + bidx) * ep.nkv + (nf - ep.nq) + g4;
+            }
+            Vec4<bf16>::store(dst, lo[0], lo[1], lo[2], lo[3]);
+            Vec4<bf16>::store(dst + 32, hi[0], hi[1], hi[2], hi[3]);
+          } else {
+            const int vn = nf - ep.nq - ep.nkv + g4;
+            const int kvh = vn >> 6, dc = vn & 63;
+            bf16* vp = reinterpret_cast<bf16*>(ep.vt) + (((size_t)bseq * ep.hkv + kvh) * 64 + dc) * ep.kpad + bidx;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vp[(size_t)e * ep.kpad] = (bf16)acc[i][j][e];
+          }
         }
       }
     }
+    if (tnext < 0) break;
+    t = tnext; m0 = nm0; n0 = nn0;
+    buf0 = (buf0 + nk) & 1;
   }
 }
 
 namespace {
 
 int g_group_m = -1;       // tuning override of the tile-order group (MOR_GEMM_GROUP_M)
+
+// Workgroups of a launch: at most one per tile, and at most as many as are resident at once
+// (256 CUs x per_cu), each then taking several tiles. MOR_GEMM_PERSIST=0 gives every tile its
+// own workgroup instead (read at every launch, for measurement).
+int grid_size(int ntiles, int per_cu) {
+  const char* e = getenv("MOR_GEMM_PERSIST");
+  if (e && atoi(e) == 0) return ntiles;
+  return std::min(ntiles, 256 * per_cu);
+}
 
 int group_m() {
   if (g_group_m == -1) {
@@ -288,10 +334,11 @@ hipError_t launch_cfg(int epi, const bf16* A, const bf16* W, int N, int K, int m
   const int nblk = tn * tm;
   if (nblk == 0) return hipSuccess;
   const int gm = group_m();
+  const dim3 grid(grid_size(nblk, BN * BM <= 128 * 192 ? 2 : 1));
   switch (epi) {
-    case EPI_QKV: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_QKV>), dim3(nblk), dim3(256), 0, s, A, W, N, K, tn, gm, meta, ep); break;
-    case EPI_RESID: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_RESID>), dim3(nblk), dim3(256), 0, s, A, W, N, K, tn, gm, meta, ep); break;
-    default: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_SWIGLU>), dim3(nblk), dim3(256), 0, s, A, W, N, K, tn, gm, meta, ep); break;
+    case EPI_QKV: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_QKV>), grid, dim3(256), 0, s, A, W, N, K, tn, nblk, gm, meta, ep); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_RESID>), grid, dim3(256), 0, s, A, W, N, K, tn, nblk, gm, meta, ep); break;
+    default: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_SWIGLU>), grid, dim3(256), 0, s, A, W, N, K, tn, nblk, gm, meta, ep); break;
   }
   return hipGetLastError();
 }
@@ -303,7 +350,7 @@ hipError_t launch_cfg_rs(const bf16* A, const bf16* W, int N, int K, int m_upper
   const int tn = (N + BN - 1) / BN, tm = (m_upper + BM - 1) / BM;
   const int nblk = tn * tm;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI>), dim3(nblk), dim3(256), 0, s, A, W, N, K, tn, group_m(), meta, ep);
+  hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI>), dim3(grid_size(nblk, 2)), dim3(256), 0, s, A, W, N, K, tn, nblk, group_m(), meta, ep);
   return hipGetLastError();
 }
 
@@ -315,10 +362,11 @@ hipError_t launch_cfg8(int epi, const bf16* A, const bf16* W, int N, int K, int 
   const int nblk = tn * tm;
   if (nblk == 0) return hipSuccess;
   const int gm = group_m();
+  const dim3 grid(grid_size(nblk, BN * BM <= 128 * 192 ? 2 : 1));
   switch (epi) {
-    case EPI_QKV: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_QKV, 4>), dim3(nblk), dim3(512), 0, s, A, W, N, K, tn, gm, meta, ep); break;
-    case EPI_RESID: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_RESID, 4>), dim3(nblk), dim3(512), 0, s, A, W, N, K, tn, gm, meta, ep); break;
-    default: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_SWIGLU, 4>), dim3(nblk), dim3(512), 0, s, A, W, N, K, tn, gm, meta, ep); break;
+    case EPI_QKV: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_QKV, 4>), grid, dim3(512), 0, s, A, W, N, K, tn, nblk, gm, meta, ep); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_RESID, 4>), grid, dim3(512), 0, s, A, W, N, K, tn, nblk, gm, meta, ep); break;
+    default: hipLaunchKernelGGL((k_gemm_bf16<BN, BM, EPI_SWIGLU, 4>), grid, dim3(512), 0, s, A, W, N, K, tn, nblk, gm, meta, ep); break;
   }
   return hipGetLastError();
 }
