@@ -290,12 +290,18 @@ namespace {
 int g_group_m = -1;       // tuning override of the tile-order group (MOR_GEMM_GROUP_M)
 
 // Workgroups of a launch: at most one per tile, and at most as many as are resident at once
-// (256 CUs x per_cu), each then taking several tiles. MOR_GEMM_PERSIST=0 gives every tile its
-// own workgroup instead (read at every launch, for measurement).
+// (256 CUs x per_cu), each then taking several tiles. Read at every launch: MOR_GEMM_PERSIST=0
+// gives every tile its own workgroup (for measurement); MOR_GEMM_PERSIST=n caps the grid at n
+// rounded up to a multiple of 8 (tests: many tiles per workgroup at small sizes). A grid smaller
+// than the tile count is always a multiple of 8, so that every XCD owning tiles has workgroups.
 int grid_size(int ntiles, int per_cu) {
-  const char* e = getenv("MOR_GEMM_PERSIST");
-  if (e && atoi(e) == 0) return ntiles;
-  return std::min(ntiles, 256 * per_cu);
+  int cap = 256 * per_cu;
+  if (const char* e = getenv("MOR_GEMM_PERSIST")) {
+    const int v = atoi(e);
+    if (v <= 0) return ntiles;
+    cap = std::max(8, (v + 7) / 8 * 8);
+  }
+  return std::min(ntiles, cap);
 }
 
 int group_m() {

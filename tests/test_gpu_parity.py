@@ -78,6 +78,18 @@ def test_small_bf16_forced_gemm_tiles(tile, monkeypatch):
     _compare_prefill(workload.get_config("small_bf16"))
 
 
+@pytest.mark.parametrize("persist,tile", [("8", None), ("8", "128x64"), ("16", "256x256w8"),
+                                          ("0", None)])
+def test_small_bf16_persistent_gemm_grids(persist, tile, monkeypatch):
+    """The projection GEMM's workgroups take several tiles each (grid capped at 8 or 16
+    workgroups, so every workgroup prefetches its next tiles across both LDS stage parities:
+    K = 192 gives 3 stages, K = 512 gives 8), and one workgroup per tile (0)."""
+    monkeypatch.setenv("MOR_GEMM_PERSIST", persist)
+    if tile:
+        monkeypatch.setenv("MOR_GEMM_TILE", tile)
+    _compare_prefill(workload.get_config("small_bf16"))
+
+
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (8, 2)])
 def test_small_bf16_gqa_ratios(hq, hkv):
     """bf16 attention with 1, 2 and 4 query heads per KV head (the 360M shape has 3)."""
