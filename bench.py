@@ -117,22 +117,65 @@ def decode_traffic_from_profile():
     return rec.get("bytes_per_iteration")
 
 
-def cpu_baseline(cfg, weights, H0_np, seq_len: int):
-    """The oracle, as it stands, on one sequence of the same workload (host cores)."""
-    import numpy as np
-    import oracle
+def host_threads_and_cpu():
+    """BLAS threads the oracle runs with, and the host CPU model."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return int(threads), model
+
+
+def cpu_baseline(cfg, weights, H0_np, seq_len: int):
+    """The oracle, as it stands, on one sequence of the same workload (host cores)."""
+    import numpy as np
+    import oracle
+    threads, cpu = host_threads_and_cpu()
     x = np.ascontiguousarray(H0_np[:1, :seq_len])
     t0 = time.perf_counter()
     oracle.prefill(cfg.replace(seq=seq_len), weights, x)
     dt = time.perf_counter() - t0
-    return {"value": seq_len / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": seq_len / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"1 of {cfg.batch} sequences ({seq_len} tokens) of the same prefill, "
-                      f"oracle in float64 with bf16 storage points; {dt:.1f} s"}
+                      f"oracle in float64 with bf16 storage points; {dt:.1f} s on {cpu}, "
+                      f"{len(os.sched_getaffinity(0))} cores available"}
+
+
+def decode_cpu_baseline(budget_s: float = 10.0):
+    """The oracle's token-by-token decode (per-recursion caches), as it stands, on the first
+    requests of the same MoR-4 decode workload, in order, until about budget_s seconds of host
+    time are spent (the request that crosses the budget is finished)."""
+    import numpy as np
+    import oracle
+    import workload
+
+    threads, cpu = host_threads_and_cpu()
+    cfg = workload.get_config("smol360m_mor4_decode")
+    W = workload.make_weights(cfg)
+    with open(os.path.join(ROOT, "tests", "golden", "decode_router_bias.json")) as f:
+        W["router_b"] = np.array(json.load(f)["router_b"], np.float32)
+    lens = workload.make_decode_lengths(cfg)
+    xs = workload.make_decode_inputs(cfg, lens)
+    tok, n, t0 = 0, 0, time.perf_counter()
+    while n < min(64, len(lens)) and time.perf_counter() - t0 < budget_s:
+        oracle.decode_sequence(cfg, W, xs[n])
+        tok += int(lens[n])
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the first {n} of {len(lens)} requests ({tok} tokens) of the same decode "
+                      f"workload, one at a time, oracle in float64 with bf16 storage points; "
+                      f"{dt:.1f} s on {cpu}"}
 
 
 def decode_bench(args, kv_mode="recursion"):
@@ -395,6 +438,8 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, W, H0, args.cpu_seq)
+        if not args.no_decode:
+            result["decode"]["cpu_baseline"] = decode_cpu_baseline()
     print(json.dumps(result), flush=True)
 
 
