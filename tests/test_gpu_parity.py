@@ -189,6 +189,27 @@ def test_kv_cache_contents():
     model.close()
 
 
+@pytest.mark.parametrize("name", ["small_bf16", "small_f32"])
+def test_prefill_in_place_equals_out_of_place(name):
+    """h_out == h_in (the input overwritten by the output) gives bitwise the result of a separate
+    output buffer, where the first layer reads the input buffer and writes the stream; the
+    input buffer is left untouched in the second case."""
+    import torch
+    cfg = workload.get_config(name)
+    model, W = build_gpu(cfg)
+    H0 = workload.make_inputs(cfg)
+    h_in = torch.from_numpy(np.ascontiguousarray(H0, np.float32)).cuda()
+    keep = h_in.clone()
+    out = model.prefill(h_in)
+    torch.cuda.synchronize()
+    assert torch.equal(h_in, keep), "the input buffer was written"
+    h2 = keep.clone()
+    model.prefill(h2, h2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, h2)
+    model.close()
+
+
 def test_determinism_bitwise():
     import torch
     cfg = workload.get_config("small_bf16")
