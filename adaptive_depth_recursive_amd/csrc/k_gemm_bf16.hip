@@ -64,16 +64,20 @@ __global__ __launch_bounds__(128 * NWM, (NWM == 4 && BN * BM <= 128 * 192) ? 2 :
   // and each takes a sequence of tiles. The hardware deals workgroups round-robin over the 8
   // XCDs (each with its own L2), so XCD x owns one contiguous range of the tile order and its
   // workgroups take that range's tiles in turn (round k of an XCD covers consecutive tiles).
+  // The row count M is known only here (the host sizes the grid for its upper bound, e.g. under
+  // token choice): only the row-blocks that hold rows are dealt out, so every XCD gets its share
+  // of the real tiles.
   const int G = gridDim.x, bid = blockIdx.x;
   const int xcd = bid % 8, slot = bid / 8;
   const int wpx = G / 8 + (xcd < G % 8 ? 1 : 0);            // workgroups on this XCD
-  const int tpx = ntiles / 8, trem = ntiles % 8;
+  const int tiles_m = min(ntiles / tiles_n, (M + BM - 1) / BM);
+  const int ntv = tiles_m * tiles_n;
+  const int tpx = ntv / 8, trem = ntv % 8;
   const int tbase = xcd < trem ? xcd * (tpx + 1) : trem * (tpx + 1) + (xcd - trem) * tpx;
   const int tend = tbase + tpx + (xcd < trem ? 1 : 0);
   // Tile order: groups of group_m activation row-blocks, swept one weight column-block at a
   // time with the row-blocks fastest, so the workgroups resident on an XCD share a few
   // activation slabs and a few weight slabs in its L2.
-  const int tiles_m = ntiles / tiles_n;
   const int gsz = group_m * tiles_n;
   // the next tile of this workgroup at or after position t that has rows (m0 < M); -1 if none
   auto next_tile = [&](int t, int& m0, int& n0) -> int {
