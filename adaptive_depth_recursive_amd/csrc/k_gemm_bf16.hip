@@ -402,11 +402,15 @@ constexpr TileCfg kTiles[] = {{128, 128, 2, 1.0, 3}, {128, 192, 2, 1.25, 5}, {19
                               {128, 96, 2, 0.92, 6}, {256, 256, 1, 1.9, 10}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-int choose_tile(int epi, int N, int m_upper) {
+// rows_bound: m_upper only bounds the rows (they are counted on the device); a tile of one
+// workgroup per CU would then leave most CUs idle when the real count is well below the bound,
+// so only the two-per-CU tiles compete.
+int choose_tile(int epi, int N, int m_upper, bool rows_bound) {
   int best = 0;
   double best_t = 1e300;
   for (int c = 0; c < kNumTiles; ++c) {
     if (kTiles[c].bn == 192 && epi == EPI_QKV) continue;   // the QKV epilogue needs 64-wide halves
+    if (rows_bound && kTiles[c].per_cu < 2) continue;
     const long tiles = (long)((N + kTiles[c].bn - 1) / kTiles[c].bn) * ((m_upper + kTiles[c].bm - 1) / kTiles[c].bm);
     const long slots = 256L * kTiles[c].per_cu;
     const double t = (double)((tiles + slots - 1) / slots) * kTiles[c].round_cost;
@@ -423,7 +427,7 @@ hipError_t launch_gemm<bf16>(int epi, const bf16* A, const bf16* W, int N, int K
   if (K % 64 || N % 64) return hipErrorInvalidValue;
   int choice = forced_tile();
   if (choice == 0) {
-    choice = choose_tile(epi, N, m_upper);
+    choice = choose_tile(epi, N, m_upper, ep.rows_bound != 0);
     // 128 x 192 also runs as eight waves at two workgroups per CU (114 VGPRs, four waves per
     // SIMD): 2-6% faster for the QKV and residual epilogues, about 1% slower for SwiGLU
     if (choice == 5 && epi != EPI_SWIGLU) choice = 11;

@@ -320,6 +320,7 @@ struct RowSet {
   const int* rows;     // 4 x [MT] pos/src/seq/idx
   int m_upper;         // grid bound on the row count
   int max_per_seq;     // grid bound on rows per sequence
+  bool exact;          // m_upper is the row count itself (not only a bound known on the host)
 };
 struct KeySet {
   const void* k;
@@ -362,6 +363,7 @@ mor_status run_layer(mor_handle_s* h, const BlockPacked& w, float* X, const RowS
   HIPCHK(launch_rmsnorm<E>(x_in ? x_in : X, d, rs.meta, rs.m_upper, w.g_attn, c.rms_eps, Xn, s));
 
   GemmEpi ep{};
+  ep.rows_bound = !rs.exact;
   ep.q = h->Q; ep.ldq = h->nq;
   ep.k = k_dst; ep.vt = vt_dst;
   ep.nq = h->nq; ep.nkv = h->nkv; ep.hd = c.head_dim; ep.hkv = c.n_kv_heads; ep.kpad = h->kpad;
@@ -385,6 +387,7 @@ mor_status run_layer(mor_handle_s* h, const BlockPacked& w, float* X, const RowS
   }
 
   GemmEpi er{};
+  er.rows_bound = !rs.exact;
   er.x = X; er.ldx = d;
   er.xin = x_in;
   {
@@ -394,6 +397,7 @@ mor_status run_layer(mor_handle_s* h, const BlockPacked& w, float* X, const RowS
   er.xin = nullptr;
   HIPCHK(launch_rmsnorm<E>(X, d, rs.meta, rs.m_upper, w.g_ffn, c.rms_eps, Xn, s));
   GemmEpi eg{};
+  eg.rows_bound = !rs.exact;
   eg.h = h->Hf; eg.ldh = dff;
   {
     TimedLaunch t(h, KIND_GATE_UP, s);
@@ -434,7 +438,7 @@ mor_status prefill_impl(mor_handle_s* h, const float* h_in, int B, int T, float*
   if (logits && c.routing != MOR_ROUTE_TOKEN_CHOICE)
     HIPCHK(launch_fill_f32(h->z + MT, R * MT, NAN, s));
 
-  const RowSet all{meta_r[0], cnt_r(0), h->rows_all, (int)BT, T};
+  const RowSet all{meta_r[0], cnt_r(0), h->rows_all, (int)BT, T, true};
   mor_status st = MOR_OK;
   if (middle) {
     const KeySet keys_first{kv_k(h, 0), kv_vt(h, 0), act_r(0), cnt_r(0)};
@@ -463,7 +467,9 @@ mor_status prefill_impl(mor_handle_s* h, const float* h_in, int B, int T, float*
     HIPCHK(launch_gather(H, d, act_r(r), meta_r[r], B, T, m_up, gate_kind, z_r(r), h->depth,
                          h->prob, r, h->X, h->rows, h->rows + MT, h->rows + 2 * MT, h->rows + 3 * MT,
                          h->gate, s));
-    const RowSet rs{meta_r[r], cnt_r(r), h->rows, m_up, per_seq};
+    // expert choice keeps exactly k_r tokens per sequence, and recursion 1 of the threshold and
+    // token-choice routers runs every token; otherwise the count is known only on the device
+    const RowSet rs{meta_r[r], cnt_r(r), h->rows, m_up, per_seq, sel_mode == SEL_EC || r == 1};
     for (int j = 1; j <= n_s; ++j) {
       const int sid = 1 + (r - 1) * n_s + (j - 1);
       const BlockPacked& wj = h->blk[block_of(c, n_s, r, j)];

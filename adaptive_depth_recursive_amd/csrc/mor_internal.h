@@ -24,6 +24,9 @@ struct GemmEpi {
   const float* xin;
   // EPI_SWIGLU
   void* h; int ldh;
+  // host side: the launch's row count is only an upper bound (the rows are counted on the
+  // device), so the tile choice avoids tiles of one workgroup per CU
+  int rows_bound;
 };
 
 // Row-set descriptor ("meta"): meta[0] = total rows M, meta[1 + b] = first row of sequence b.
