@@ -21,13 +21,19 @@ The residual stream is kept in float64 here (the library keeps it in fp32).
 Router logits are decisions, so they are computed in fp32 in the one fixed order
 documented at ``router_logits_fp32`` (the same order the library uses).
 
-Parity status:
+Parity status (pins in tests/test_oracle_pins.py):
+  bf16_round: bitwise against torch's float32 -> bfloat16 conversion (random values,
+  exact ties on even and odd kept bits, subnormals, the largest finite values,
+  infinities, NaN payloads).
   layer_map, capacity_counts, select_topk, attention, block, prefill (expert-choice,
-  recursion-wise and shared KV), threshold_forward, decode_sequence: pinned by
-  tests/test_oracle_pins.py.
-  The gated-update rule (delta reading of the expert-choice update) and the
-  token-choice update rule are readings of the pages: parity unpinned beyond the
-  special cases (gate = 1, unit gating) that the tests check.
+  token-choice, recursion-wise and shared KV, every sharing scheme), threshold_forward,
+  decode_sequence, sigmoid: pinned.
+  The expert-choice gated update at real gates in (0, 1) and the token-choice update at
+  the chosen depth are pinned to a transformers Llama stack run on the routed tokens and
+  combined by the update formula as read here (H + g (F(H) - H), F the n_s-layer block,
+  one gate per token per recursion). These pins fix the oracle to that reading; the
+  reading itself (the pages print g f(H) + H, and the token-choice formula is garbled)
+  is a choice, listed with the other readings where the design is documented.
 """
 from __future__ import annotations
 
@@ -50,12 +56,20 @@ __all__ = [
 def bf16_round(x) -> np.ndarray:
     """Nearest bfloat16 value of ``x`` (ties to even), returned as float64.
 
-    The value is first taken to float32, then its low 16 bits are rounded away.
+    The value is first taken to float32, then its low 16 bits are rounded away: adding
+    0x7FFF plus the lowest kept bit and truncating rounds to nearest with ties to the even
+    neighbour, also for subnormals, and carries into the exponent (the largest finite
+    values round up to infinity). A NaN stays a NaN (the carry would turn some NaN
+    payloads into an infinity or a zero).
     """
     f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
     u = f.view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):                # signalling-NaN payloads
+        r = u.astype(np.uint32).view(np.float32).astype(np.float64)
+    nan = np.isnan(f)
+    r[nan] = np.nan
+    return r
 
 
 def _store(x: np.ndarray, bf16: bool) -> np.ndarray:
@@ -288,8 +302,8 @@ def shared_schedule(cfg) -> List[List[int]]:
 def _prefill_one(cfg, W, h0, ks, forced, gate_mode, update):
     T = h0.shape[0]
     pos_all = np.arange(T)
-    R, n_s = cfg.n_rec, cfg.n_shared
     sched = shared_schedule(cfg)
+    R, n_s = cfg.n_rec, len(sched[0])
     middle = getattr(cfg, "sharing", "middle_cycle").startswith("middle")
     if middle:
         H, kv_first = block(W["first"], h0, pos_all, cfg)
@@ -439,7 +453,8 @@ def decode_sequence(cfg, weights, inputs: np.ndarray, gate_mode: Optional[str] =
         raise ValueError("depth-wise decode is defined for Middle-Cycle sharing")
     W = to_f64_weights(weights)
     gm = gate_mode or cfg.gate_mode
-    R, n_s, d = cfg.n_rec, cfg.n_shared, cfg.d_model
+    R, d = cfg.n_rec, cfg.d_model
+    n_s = len(shared_schedule(cfg)[0])
     Hkv, hd = cfg.n_kv_heads, cfg.head_dim
 
     def empty():

@@ -103,11 +103,65 @@ def test_router_logit_error_bound(d):
     assert np.array_equal(zb, (z.astype(np.float32) + np.float32(0.25)))
 
 
-def test_sigmoid_closed_form():
-    z = np.array([-30.0, -2.0, 0.0, 0.5, 7.0], np.float32)
-    want = [1.0 / (1.0 + math.exp(-float(v))) for v in z]
-    assert np.allclose(oracle.sigmoid(z), want, rtol=1e-15, atol=0)
+def test_sigmoid_facts():
+    """The router gate is the logistic function: sigma(0) = 1/2, sigma(-z) = 1 - sigma(z),
+    sigma(ln 3) = 3/4, limits 0 and 1, increasing, and sigma' = sigma (1 - sigma)."""
     assert oracle.sigmoid(np.float32(0.0)) == 0.5
+    assert abs(oracle.sigmoid(math.log(3.0)) - 0.75) < 1e-15
+    z = np.linspace(-12.0, 12.0, 2401)
+    s = oracle.sigmoid(z)
+    assert np.all(np.diff(s) > 0) and np.all((s > 0) & (s < 1))
+    assert np.allclose(oracle.sigmoid(-z), 1.0 - s, rtol=0, atol=2e-16)
+    h = 1e-5
+    num = (oracle.sigmoid(z + h) - oracle.sigmoid(z - h)) / (2 * h)
+    assert np.allclose(num, s * (1 - s), rtol=1e-5, atol=1e-10)
+    assert oracle.sigmoid(60.0) == 1.0 and 0.0 < oracle.sigmoid(-60.0) < 1e-25
+
+
+# --------------------------------------------------------------------- bf16 rounding
+def _bf16_probe_values():
+    """float32 bit patterns that separate rounding rules: random magnitudes over the whole
+    exponent range, exact ties (low half 0x8000) with the kept low bit even and odd, one ulp
+    either side of a tie, subnormals, the largest finite values, zeros, infinities."""
+    rng = np.random.default_rng(11)
+    u = [rng.integers(0, 1 << 32, 20000, dtype=np.uint64).astype(np.uint32)]
+    hi = rng.integers(0, 1 << 16, 4000, dtype=np.uint64).astype(np.uint32)
+    hi = hi[((hi >> 7) & 0xFF) != 0xFF]                       # finite upper halves
+    for low in (0x8000, 0x7FFF, 0x8001, 0x0000, 0xFFFF):
+        u.append((hi << 16) | low)
+    u.append(rng.integers(0, 0x00800000, 3000, dtype=np.uint64).astype(np.uint32))   # subnormals
+    u.append(np.array([0x7F7FFFFF, 0x7F7F8000, 0x7F7F7FFF, 0x7F7E8000, 0xFF7FFFFF, 0x00008000,
+                       0x00018000, 0x00000001, 0x0, 0x80000000, 0x7F800000, 0xFF800000], np.uint32))
+    u = np.concatenate(u)
+    exp = (u >> 23) & 0xFF
+    return u[~((exp == 0xFF) & ((u & 0x7FFFFF) != 0))].view(np.float32)   # NaNs checked apart
+
+
+def test_bf16_round_equals_torch_conversion():
+    """The oracle's storage-point rounding is float32 -> bfloat16 round-to-nearest-even: bitwise
+    equal to torch's conversion on every probe value (a truncating or ties-away rounding, or a
+    missing exponent carry, differs on the tie and boundary probes)."""
+    x = _bf16_probe_values()
+    got = oracle.bf16_round(x).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # the tie cases really are ties: both neighbours are equally far
+    ties = x[(x.view(np.uint32) & 0xFFFF) == 0x8000]
+    ties = ties[np.isfinite(ties) & (np.abs(ties) < 3e38)]
+    lo = (ties.view(np.uint32) & 0xFFFF0000).view(np.float32).astype(np.float64)
+    hi = ((ties.view(np.uint32) & 0xFFFF0000) + 0x10000).view(np.float32).astype(np.float64)
+    assert np.all(np.abs(ties - lo) == np.abs(hi - ties))
+    even = (oracle.bf16_round(ties).astype(np.float32).view(np.uint32) >> 16) & 1
+    assert np.all(even == 0)
+
+
+def test_bf16_round_keeps_nan():
+    """Rounding a NaN gives a NaN, whatever its payload (the carry of the bit trick alone would
+    turn 0x7FFFFFFF into -0 and 0x7F800001 into +inf)."""
+    pats = np.array([0x7FFFFFFF, 0x7F800001, 0xFFC00000, 0x7FC00001, 0xFFFFFFFF, 0x7F80FFFF],
+                    np.uint32)
+    assert np.all(np.isnan(oracle.bf16_round(pats.view(np.float32))))
+    assert np.all(np.isnan(torch.from_numpy(pats.view(np.float32)).to(torch.bfloat16).float().numpy()))
 
 
 # --------------------------------------------------------------------- top-k
@@ -375,6 +429,81 @@ def test_token_choice_all_depth_one_special_case():
     ids = [0] + list(range(1, cfg.n_shared + 1)) + [cfg.n_shared + 1]
     ref = llama_stack(cfg, layers, ids, H0)
     assert np.allclose(res["out"], ref, rtol=HF_RTOL, atol=HF_ATOL)
+
+
+def _exact_logits(H, w):
+    return torch.from_numpy(np.asarray(H, np.float64)) @ torch.from_numpy(np.asarray(w, np.float64))
+
+
+def test_expert_choice_gated_update_with_real_gates():
+    """The expert-choice update at every recursion, with gates strictly inside (0, 1) and two
+    shared layers per recursion: starting from the oracle's own H before recursion r, the
+    routed tokens A_r (the top k_r of the exactly computed logits) run the n_s Middle-Cycle
+    layers as transformers' Llama layers at their original positions (causal over A_r), and the
+    result is merged as H + sigmoid(z) (F(H) - H) once per recursion. That must equal the
+    oracle's H after recursion r on A_r, and every other row must be untouched. A gate applied
+    per layer, the literal g F(H) + H, a dropped gate or a wrong position map all differ."""
+    cfg = workload.get_config("small_f32", seq=23, batch=1)
+    assert cfg.n_shared == 2
+    W = workload.make_weights(cfg)
+    H0 = workload.make_inputs(cfg)
+    p = oracle.prefill(cfg, W, H0)["per_seq"][0]
+    ks = oracle.capacity_counts(cfg.cap_num, cfg.cap_den, cfg.seq)
+    prev = np.arange(cfg.seq)
+    gates = []
+    for r in range(1, cfg.n_rec + 1):
+        Hp = p["hist"][r - 1]
+        z = _exact_logits(Hp[prev], W["router_w"][r - 1]).numpy()
+        order = np.argsort(-z, kind="stable")
+        sel = np.sort(prev[order[:ks[r - 1]]])
+        if ks[r - 1] < len(prev):
+            assert z[order[ks[r - 1] - 1]] - z[order[ks[r - 1]]] > 1e-6    # no near tie
+        assert np.array_equal(sel, p["sel"][r - 1])
+        g = torch.sigmoid(torch.from_numpy(z[np.searchsorted(prev, sel)])).numpy()
+        gates.append(g)
+        F = llama_stack(cfg, W["shared"], list(range(cfg.n_shared)), Hp[sel][None],
+                        position_ids=sel)[0]
+        want = Hp.copy()
+        want[sel] = Hp[sel] + g[:, None] * (F - Hp[sel])
+        got = p["hist"][r]
+        assert np.allclose(got[sel], want[sel], rtol=HF_RTOL, atol=HF_ATOL), r
+        rest = np.setdiff1d(np.arange(cfg.seq), sel)
+        assert np.array_equal(got[rest], Hp[rest]), r
+        prev = sel
+    g = np.concatenate(gates)
+    assert g.min() < 0.45 and g.max() > 0.55 and np.all((g > 0.05) & (g < 0.95))
+
+
+def test_token_choice_update_at_chosen_depth():
+    """Token choice: depth i = argmax of Theta^T H^1 (exact logits), softmax weight p_i. At each
+    recursion r the tokens with i >= r run the n_s layers (transformers Llama layers at their
+    original positions, causal over that set); a token whose chosen depth is r is merged as
+    H + p_i (F(H) - H), a token going deeper takes F(H), the others are untouched."""
+    cfg = workload.get_config("small_f32", routing="tc", seq=29, batch=1)
+    W = workload.make_weights(cfg)
+    H0 = workload.make_inputs(cfg)
+    p = oracle.prefill(cfg, W, H0)["per_seq"][0]
+    H1 = p["hist"][0]
+    Z = _exact_logits(H1, W["router_w"].T)
+    probs = torch.softmax(Z, dim=1).numpy()
+    Zs = np.sort(Z.numpy(), axis=1)
+    assert np.all(Zs[:, -1] - Zs[:, -2] > 1e-6)                    # argmax not a near tie
+    depth = np.argmax(Z.numpy(), axis=1) + 1
+    assert np.array_equal(depth, p["depth"])
+    assert len(set(depth.tolist())) == cfg.n_rec                   # every depth occurs
+    for r in range(1, cfg.n_rec + 1):
+        Hp = p["hist"][r - 1]
+        sel = np.nonzero(depth >= r)[0]
+        assert np.array_equal(sel, p["sel"][r - 1])
+        F = llama_stack(cfg, W["shared"], list(range(cfg.n_shared)), Hp[sel][None],
+                        position_ids=sel)[0]
+        stop = depth[sel] == r
+        want = Hp.copy()
+        want[sel] = np.where(stop[:, None], Hp[sel] + probs[sel, r - 1][:, None] * (F - Hp[sel]), F)
+        got = p["hist"][r]
+        assert np.allclose(got[sel], want[sel], rtol=HF_RTOL, atol=HF_ATOL), r
+        rest = np.setdiff1d(np.arange(cfg.seq), sel)
+        assert np.array_equal(got[rest], Hp[rest]), r
 
 
 def test_token_choice_sets_follow_depths():
