@@ -244,20 +244,54 @@ def test_decode_kv_pool_exhaustion_reported():
 
 def test_decode_full_size_sampled():
     """The 360M-shape MoR-4 decode workload at its launch configuration (51 slots, 64-token
-    pages): the first 80 requests of the seeded length distribution, routing checked stage-wise
-    on every token, two requests checked against the oracle (teacher-forced)."""
+    pages): the first 80 requests of the seeded length distribution, uncapped (up to 1331
+    tokens, so the longest requests' attention runs two rounds of 1024 keys per workgroup),
+    routing checked stage-wise on every token, the two longest requests and the shortest one
+    checked against the oracle (teacher-forced)."""
     cfg = workload.get_config("smol360m_mor4_decode")
     bias = np.array(_gold("decode_router_bias.json")["router_b"], np.float32)
-    lens = np.minimum(workload.make_decode_lengths(cfg)[:80], 300)
+    lens = workload.make_decode_lengths(cfg)[:80]
     model, W, lens = _setup(cfg, slots=cfg.slots, bias=bias, page=64, lengths=lens)
     inputs = workload.make_decode_inputs(cfg, lens)
     res = _run(model, cfg, lens, inputs)
     _check_routing(cfg, W, res, lens)
-    short = [int(i) for i in np.argsort(lens)[:2]]
-    say(f"[cpu] oracle on requests {short} (lengths {lens[short]})")
-    worst = _compare(cfg, W, res, lens, inputs, teacher=True, which=set(short))
+    order = np.argsort(lens, kind="stable")
+    which = [int(order[-1]), int(order[-2]), int(order[0])]
+    assert lens[which[0]] > 1024
+    say(f"[cpu] oracle on requests {which} (lengths {lens[which].tolist()})")
+    worst = _compare(cfg, W, res, lens, inputs, teacher=True, which=set(which))
     say(f"[gpu] full-size decode: {int(lens.sum())} tokens, {res['iters']} iterations, "
         f"depths {np.bincount(res['depth'], minlength=cfg.n_rec + 1)[1:]}, worst rel err {worst:.2e}")
+    model.close()
+
+
+def test_decode_long_context_bf16():
+    """A request of 1300 tokens next to short ones: the bf16 decode attention (16 waves of
+    64-key tiles, 1024 keys per round) takes two rounds from position 1024 on, and every
+    wave's next tile overwrites its LDS V tile after the current one was read. Teacher-forced
+    against the oracle at 2e-2, routing stage-wise bit-exact."""
+    cfg = workload.get_config("small_thr_bf16", max_len=1600)
+    model, W, lens = _setup(cfg, slots=3, lengths=[1300, 40, 211])
+    inputs = workload.make_decode_inputs(cfg, lens)
+    res = _run(model, cfg, lens, inputs)
+    _check_routing(cfg, W, res, lens)
+    worst = _compare(cfg, W, res, lens, inputs, teacher=True)
+    say(f"[gpu] decode bf16 long context: {res['iters']} iterations, worst rel err {worst:.2e}, "
+        f"depth histogram {np.bincount(res['depth'], minlength=cfg.n_rec + 1)[1:]}")
+    model.close()
+
+
+def test_decode_long_context_f32_free_running():
+    """fp32 decode attention runs 8 waves (512 keys per round): a 700-token request crosses into
+    the second round in the first and last layers and in the recursion-1 layers. Free-running:
+    exit depths equal the oracle's own, hidden states within 1e-4."""
+    cfg = workload.get_config("small_thr_bf16", dtype="f32", max_len=800)
+    model, W, lens = _setup(cfg, slots=3, page=32, lengths=[700, 23, 5])
+    inputs = workload.make_decode_inputs(cfg, lens)
+    res = _run(model, cfg, lens, inputs)
+    _check_routing(cfg, W, res, lens)
+    worst = _compare(cfg, W, res, lens, inputs, teacher=False)
+    say(f"[gpu] decode f32 long context: {res['iters']} iterations, worst rel err {worst:.2e}")
     model.close()
 
 
@@ -282,21 +316,27 @@ def test_decode_graph_replay_matches_eager():
     model.close()
 
 
-@pytest.mark.parametrize("dtype,kv_mode", [("f32", "recursion"), ("bf16", "recursion"), ("f32", "share")])
-def test_decode_continues_prefill(dtype, kv_mode):
-    """Prefill -> decode hand-over: three prompts of 40 tokens are prefilled with threshold
-    routing, then decoded further (5, 17 and 9 tokens) from the prefill's per-recursion caches.
-    With threshold routing (causal) the result must equal the oracle's forward of each whole
-    sequence: fp32 free-running (exact depths), bf16 teacher-forced."""
+@pytest.mark.parametrize("dtype,kv_mode,T,lens", [
+    ("f32", "recursion", 40, (5, 17, 9)), ("bf16", "recursion", 40, (5, 17, 9)),
+    ("f32", "share", 40, (5, 17, 9)), ("bf16", "recursion", 1000, (30, 12)),
+    ("f32", "share", 1000, (9, 21))])
+def test_decode_continues_prefill(dtype, kv_mode, T, lens):
+    """Prefill -> decode hand-over: prompts of T tokens are prefilled with threshold routing,
+    then decoded further from the prefill's per-recursion caches (prompts of 1000 tokens put
+    the continuation's attention past one round of keys per workgroup in every layer stream
+    that recursion 1 feeds). With threshold routing (causal) the result must equal the oracle's
+    forward of each whole sequence: fp32 free-running (exact depths), bf16 teacher-forced."""
     import torch
     import adaptive_depth_recursive_amd as mor
     cfg = workload.get_config("small_thr_bf16", dtype=dtype, kv_mode=kv_mode)
     W = workload.make_weights(cfg)
     W["router_b"] = BIAS_SMALL
-    B, T = 3, 40
-    lens = np.array([5, 17, 9], np.int32)
+    lens = np.array(lens, np.int32)
+    B = len(lens)
+    max_seq = -(-(T + int(lens.max())) // 64) * 64
     say(f"[gpu] decode hand-over {dtype} {kv_mode}: prefill {B} x {T}, continue {lens.tolist()}")
-    model = mor.Mor(cfg, W, max_batch=B, max_seq=64, max_slots=B, kv_page_tokens=16, max_requests=B)
+    model = mor.Mor(cfg, W, max_batch=B, max_seq=max_seq, max_slots=B, kv_page_tokens=16,
+                    max_requests=B)
     prompt = workload.make_inputs(cfg, batch=B, seq=T)
     pre = model.prefill_outputs(torch.from_numpy(prompt).cuda(), debug=False)
     torch.cuda.synchronize()
