@@ -107,7 +107,8 @@ EXPORTED = ("mor_abi_version", "mor_last_error", "mor_workspace_bytes", "mor_ini
             "mor_prefill", "mor_route", "mor_kv_view", "mor_get_error_flags", "mor_timing_enable",
             "mor_timing_read", "mor_decode_submit", "mor_decode_continue", "mor_decode_step", "mor_decode_stats",
             "mor_destroy")
-KERNEL_KINDS = {"qkv": 1, "attention": 2, "o_proj": 3, "gate_up": 4, "down": 5}
+KERNEL_KINDS = {"qkv": 1, "attention": 2, "o_proj": 3, "gate_up": 4, "down": 5, "router": 6,
+                "select": 7, "gather": 8, "scatter": 9, "rmsnorm": 10}
 
 
 def _check(status: int):

@@ -329,7 +329,8 @@ struct KeySet {
   const int* kcnt;     // [B]
 };
 
-enum { KIND_QKV = 1, KIND_ATTN = 2, KIND_O = 3, KIND_GATE_UP = 4, KIND_DOWN = 5 };
+enum { KIND_QKV = 1, KIND_ATTN = 2, KIND_O = 3, KIND_GATE_UP = 4, KIND_DOWN = 5, KIND_ROUTER = 6,
+       KIND_SELECT = 7, KIND_GATHER = 8, KIND_SCATTER = 9, KIND_NORM = 10, KIND_LAST = KIND_NORM };
 
 // Brackets one launch with a pair of events when this kind is being timed.
 struct TimedLaunch {
@@ -360,7 +361,10 @@ mor_status run_layer(mor_handle_s* h, const BlockPacked& w, float* X, const RowS
   const mor_config& c = h->cfg;
   const int d = c.d_model, dff = c.d_ff, MT = (int)h->MT;
   E* Xn = reinterpret_cast<E*>(h->Xn);
-  HIPCHK(launch_rmsnorm<E>(x_in ? x_in : X, d, rs.meta, rs.m_upper, w.g_attn, c.rms_eps, Xn, s));
+  {
+    TimedLaunch t(h, KIND_NORM, s);
+    HIPCHK(launch_rmsnorm<E>(x_in ? x_in : X, d, rs.meta, rs.m_upper, w.g_attn, c.rms_eps, Xn, s));
+  }
 
   GemmEpi ep{};
   ep.rows_bound = !rs.exact;
@@ -395,7 +399,10 @@ mor_status run_layer(mor_handle_s* h, const BlockPacked& w, float* X, const RowS
     HIPCHK(launch_gemm<E>(EPI_RESID, reinterpret_cast<const E*>(h->O), reinterpret_cast<const E*>(w.wo), d, h->nq, rs.m_upper, rs.meta, er, s));
   }
   er.xin = nullptr;
-  HIPCHK(launch_rmsnorm<E>(X, d, rs.meta, rs.m_upper, w.g_ffn, c.rms_eps, Xn, s));
+  {
+    TimedLaunch t(h, KIND_NORM, s);
+    HIPCHK(launch_rmsnorm<E>(X, d, rs.meta, rs.m_upper, w.g_ffn, c.rms_eps, Xn, s));
+  }
   GemmEpi eg{};
   eg.rows_bound = !rs.exact;
   eg.h = h->Hf; eg.ldh = dff;
@@ -449,24 +456,33 @@ mor_status prefill_impl(mor_handle_s* h, const float* h_in, int B, int T, float*
   if (h_per_rec) HIPCHK(hipMemcpyAsync(h_per_rec, H, hbytes, hipMemcpyDeviceToDevice, s));
 
   const bool tc = c.routing == MOR_ROUTE_TOKEN_CHOICE;
-  if (tc) {
-    HIPCHK(launch_router_tc(H, d, (int)BT, h->router_w, R, h->tc_logits, h->depth, h->prob, s));
-  } else {
-    HIPCHK(launch_router(H, d, h->rows_all + MT, meta_r[0], (int)BT, h->router_w,
-                         h->has_bias ? h->router_b : nullptr, z_r(1), s));
+  {
+    TimedLaunch t(h, KIND_ROUTER, s);
+    if (tc) {
+      HIPCHK(launch_router_tc(H, d, (int)BT, h->router_w, R, h->tc_logits, h->depth, h->prob, s));
+    } else {
+      HIPCHK(launch_router(H, d, h->rows_all + MT, meta_r[0], (int)BT, h->router_w,
+                           h->has_bias ? h->router_b : nullptr, z_r(1), s));
+    }
   }
   const int sel_mode = c.routing == MOR_ROUTE_EC_TOPK ? SEL_EC
                        : c.routing == MOR_ROUTE_THRESHOLD ? SEL_THRESHOLD : SEL_TC;
   const int gate_kind = c.gate_mode == MOR_GATE_UNIT ? GATE_ASSIGN : tc ? GATE_TC : GATE_SIGMOID;
   for (int r = 1; r <= R; ++r) {
-    HIPCHK(launch_select(sel_mode, B, T, z_r(r), h->depth, act_r(r - 1), cnt_r(r - 1), ks[r - 1], r,
-                         act_r(r), cnt_r(r), h->err, s));
+    {
+      TimedLaunch t(h, KIND_SELECT, s);
+      HIPCHK(launch_select(sel_mode, B, T, z_r(r), h->depth, act_r(r - 1), cnt_r(r - 1), ks[r - 1], r,
+                           act_r(r), cnt_r(r), h->err, s));
+    }
     HIPCHK(launch_offsets(cnt_r(r), B, meta_r[r], s));
     const int per_seq = sel_mode == SEL_EC ? std::min(ks[r - 1], T) : T;
     const int m_up = B * per_seq;
-    HIPCHK(launch_gather(H, d, act_r(r), meta_r[r], B, T, m_up, gate_kind, z_r(r), h->depth,
-                         h->prob, r, h->X, h->rows, h->rows + MT, h->rows + 2 * MT, h->rows + 3 * MT,
-                         h->gate, s));
+    {
+      TimedLaunch t(h, KIND_GATHER, s);
+      HIPCHK(launch_gather(H, d, act_r(r), meta_r[r], B, T, m_up, gate_kind, z_r(r), h->depth,
+                           h->prob, r, h->X, h->rows, h->rows + MT, h->rows + 2 * MT, h->rows + 3 * MT,
+                           h->gate, s));
+    }
     // expert choice keeps exactly k_r tokens per sequence, and recursion 1 of the threshold and
     // token-choice routers runs every token; otherwise the count is known only on the device
     const RowSet rs{meta_r[r], cnt_r(r), h->rows, m_up, per_seq, sel_mode == SEL_EC || r == 1};
@@ -486,8 +502,11 @@ mor_status prefill_impl(mor_handle_s* h, const float* h_in, int B, int T, float*
     }
     const float* w_next = (!tc && r < R) ? h->router_w + (size_t)r * d : nullptr;
     const float* b_next = (w_next && h->has_bias) ? h->router_b + r : nullptr;
-    HIPCHK(launch_scatter(H, h->X, d, meta_r[r], m_up, h->rows + MT, h->gate, w_next, b_next,
-                          z_r(r + 1 <= R ? r + 1 : R), s));
+    {
+      TimedLaunch t(h, KIND_SCATTER, s);
+      HIPCHK(launch_scatter(H, h->X, d, meta_r[r], m_up, h->rows + MT, h->gate, w_next, b_next,
+                            z_r(r + 1 <= R ? r + 1 : R), s));
+    }
     if (h_per_rec)
       HIPCHK(hipMemcpyAsync(h_per_rec + (size_t)r * BT * d, H, hbytes, hipMemcpyDeviceToDevice, s));
   }
@@ -877,7 +896,7 @@ mor_status mor_decode_stats(mor_handle* h, void* stream, int64_t* out) {
 
 mor_status mor_timing_enable(mor_handle* h, int32_t kind, int32_t max_launches) {
   if (!h) return fail(MOR_E_INVALID, "null handle");
-  if (kind < 0 || kind > KIND_DOWN || max_launches < 0) return fail(MOR_E_INVALID, "kind or max_launches");
+  if (kind < 0 || kind > KIND_LAST || max_launches < 0) return fail(MOR_E_INVALID, "kind or max_launches");
   for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
   h->ev.clear();
   h->ev_used = 0;

@@ -74,6 +74,79 @@ def flop_counts(cfg, counts, sel_pos=None):
             "gate_up_launches": 2 + R * n_s}
 
 
+def memory_kernel_bytes(cfg, counts):
+    """Algorithmic HBM bytes of one call's memory-bound kernels, from the realised counts
+    counts[r][b]: the router logits of recursion 1 read every row of H (4 B per element) and
+    write one logit per token; the selector reads a logit and a position per token active
+    before the recursion and writes the kept positions; the gather reads a row of H and writes
+    it to the compacted buffer (8 B per element); the gated scatter reads H and the compacted
+    row and writes H (12 B per element); an RMSNorm reads fp32 rows and writes bf16 ones
+    (4 + 2 B per element), twice per layer. Returns {kind: (bytes per call, launches per call)}."""
+    B, T, R, d = counts.shape[1], cfg.seq, cfg.n_rec, cfg.d_model
+    n_s = cfg.n_shared
+    es = 2 if cfg.dtype == "bf16" else 4
+    BT = B * T
+    prev = [BT] + [int(counts[r].sum()) for r in range(R - 1)]
+    M = [int(counts[r].sum()) for r in range(R)]
+    router_rows = BT * (R if cfg.routing == "tc" else 1)
+    rows_normed = 2 * BT * 2 + 2 * n_s * sum(M)
+    return {
+        "router": (BT * d * 4 + router_rows * 4, 1),
+        "select": (sum(8 * p + 4 * m for p, m in zip(prev, M)), R),
+        "gather": (sum(8 * m * d for m in M), R),
+        "scatter": (sum(12 * m * d for m in M), R),
+        "rmsnorm": (rows_normed * d * (4 + es), 2 * (2 + R * n_s)),
+    }
+
+
+def time_kernel_kind(model, kind, h, h_out, steps, launches_per_call):
+    """Average launch duration (s) of one kernel kind over `steps` calls, by HIP events on the
+    library's stream around every launch of that kind."""
+    import torch
+    model.timing_enable(kind, launches_per_call * steps)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        model.prefill(h, h_out)
+    torch.cuda.synchronize()
+    k_ms, k_n = model.timing_read()
+    model.timing_enable("", 0)
+    return (k_ms / 1e3) / max(k_n, 1), k_n
+
+
+def prefill_variant(name, steps, warmup):
+    """ms per call, tokens/s and the whole call's share of the bf16 MFMA peak of another prefill
+    workload (135M shape; 360M token choice; 360M recursive KV sharing)."""
+    import torch
+    import adaptive_depth_recursive_amd as mor
+    import workload
+    cfg = workload.get_config(name)
+    W = workload.make_weights(cfg)
+    model = mor.Mor(cfg, W)
+    h = torch.from_numpy(workload.make_inputs(cfg)).cuda()
+    h_out = torch.empty_like(h)
+    outs = model.prefill_outputs(h, debug=False)
+    torch.cuda.synchronize()
+    counts = outs["counts"].cpu().numpy()
+    fl = flop_counts(cfg, counts, outs["sel_pos"].cpu().numpy())
+    del outs
+    for _ in range(warmup):
+        model.prefill(h, h_out)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(steps):
+        model.prefill(h, h_out)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    model.close()
+    return {"workload": f"{name}: batch {cfg.batch} x seq {cfg.seq}, d {cfg.d_model}, routing "
+                        f"{cfg.routing}, {cfg.kv_mode}-wise KV",
+            "ms_per_call": ms, "tokens_per_s": cfg.batch * cfg.seq / ms * 1e3,
+            "call_flops": fl["total"], "tokens_per_recursion": counts.sum(axis=1).tolist(),
+            "mfma_frac": fl["total"] / (ms / 1e3) / PEAK_BF16}
+
+
 def source_hash(path: str) -> str:
     with open(os.path.join(ROOT, path), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -118,12 +191,16 @@ def decode_traffic_from_profile():
 
 
 def host_threads_and_cpu():
-    """BLAS threads the oracle runs with, and the host CPU model."""
+    """BLAS threads the oracle runs with (set to the cores this process may run on), and the
+    host CPU model."""
+    threads = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threadpool_limits(limits=threads, user_api="blas")
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [threads])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        pass
     model = "unknown CPU"
     try:
         with open("/proc/cpuinfo") as f:
@@ -136,18 +213,19 @@ def host_threads_and_cpu():
     return int(threads), model
 
 
-def cpu_baseline(cfg, weights, H0_np, seq_len: int):
-    """The oracle, as it stands, on one sequence of the same workload (host cores)."""
+def cpu_baseline(cfg, weights, H0_np, seq_len: int, n_seq: int = 1):
+    """The oracle, as it stands, on the first n_seq sequences of the same workload (host cores)."""
     import numpy as np
     import oracle
     threads, cpu = host_threads_and_cpu()
-    x = np.ascontiguousarray(H0_np[:1, :seq_len])
+    x = np.ascontiguousarray(H0_np[:n_seq, :seq_len])
     t0 = time.perf_counter()
     oracle.prefill(cfg.replace(seq=seq_len), weights, x)
     dt = time.perf_counter() - t0
-    return {"value": seq_len / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"1 of {cfg.batch} sequences ({seq_len} tokens) of the same prefill, "
-                      f"oracle in float64 with bf16 storage points; {dt:.1f} s on {cpu}, "
+    prec = "float64 with bf16 storage points" if cfg.dtype == "bf16" else "float64"
+    return {"value": n_seq * seq_len / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_seq} of {cfg.batch} sequences ({n_seq * seq_len} tokens) of the {cfg.name} "
+                      f"prefill, oracle in {prec}; {dt:.1f} s on {cpu}, BLAS threads set to the "
                       f"{len(os.sched_getaffinity(0))} cores available"}
 
 
@@ -315,6 +393,8 @@ def main():
     ap.add_argument("--handoff-only", action="store_true", help="only the prefill -> decode hand-over leg")
     ap.add_argument("--decode-kv", default="recursion", choices=["recursion", "share"],
                     help="KV mode of --decode-only")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the 135M, token-choice and KV-sharing prefill measurements")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -407,7 +487,20 @@ def main():
                 "achieved": achieved, "peak": peak / 1e12, "unit": "TFLOP/s",
                 "frac": (achieved * 1e12 / peak) if achieved else None, "traffic": traffic,
                 "avg_launch_us": k_avg_s * 1e6, "launches_timed": k_n,
-                "flops_per_launch": k_flops_per_launch}
+                "flops_per_launch": k_flops_per_launch,
+                "call_achieved": fl["total"] / step_s / 1e12,
+                "call_frac": fl["total"] / step_s / peak,
+                "note": "achieved/frac: the dominant kernel per launch; call_achieved/call_frac: the "
+                        "whole prefill call (all kernels, algorithmic FLOPs) against the same peak"}
+
+    # memory-bound kernels of the call: algorithmic bytes against HBM
+    mem = {}
+    for mk, (byts, nl) in memory_kernel_bytes(cfg, counts).items():
+        avg_s, n = time_kernel_kind(model, mk, h, h_out, args.steps, nl)
+        bpl = byts / nl
+        mem[mk] = {"avg_launch_us": avg_s * 1e6, "launches_per_call": nl,
+                   "bytes_per_launch": bpl, "GB_per_s": bpl / avg_s / 1e9,
+                   "hbm_frac": bpl / avg_s / PEAK_HBM}
 
     result = {
         "metric": "MoR prefill tokens/sec (360M-shape, N_r=3, bf16) + % of bf16 MFMA peak",
@@ -425,10 +518,16 @@ def main():
         "wall_s_timed": wall,
         "ms_per_step_with_kernel_events": ms_ev / args.steps,
         "roofline": roofline,
+        "memory_kernels": mem,
     }
     model.close()
     del h, h_out
     torch.cuda.empty_cache()
+    if not args.no_variants:
+        result["prefill_variants"] = {
+            v: prefill_variant(v, args.steps, args.warmup)
+            for v in ("smol135m_bf16", "smol360m_tc_bf16", "smol360m_share_bf16")}
+        torch.cuda.empty_cache()
     if not args.no_decode:
         result["decode"] = decode_bench(args, "recursion")
         torch.cuda.empty_cache()
@@ -438,6 +537,13 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, W, H0, args.cpu_seq)
+        if cfg.name == "smol360m_bf16":
+            others = {}
+            for name, nseq in (("tiny_f32", 2), ("smol135m_bf16", 1)):
+                c2 = workload.get_config(name)
+                others[name] = cpu_baseline(c2, workload.make_weights(c2), workload.make_inputs(c2),
+                                            c2.seq, nseq)
+            result["cpu_baseline_other_prefills"] = others
         if not args.no_decode:
             result["decode"]["cpu_baseline"] = decode_cpu_baseline()
     print(json.dumps(result), flush=True)

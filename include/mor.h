@@ -187,8 +187,11 @@ mor_status mor_kv_view(mor_handle* h, int32_t stream, const void** k, const void
 mor_status mor_get_error_flags(mor_handle* h, void* stream, uint32_t* flags);
 
 /* Measurement hooks. mor_timing_enable makes later calls record a pair of HIP events, on the
- * call's stream, around every launch of one kernel kind: 1 QKV projection, 2 attention,
- * 3 output projection, 4 gate/up projection (SwiGLU), 5 down projection; 0 turns it off.
+ * call's stream, around every launch of one kernel kind of mor_prefill: 1 QKV projection,
+ * 2 attention, 3 output projection, 4 gate/up projection (SwiGLU), 5 down projection, 6 router
+ * logits of recursion 1 (all tokens; token-choice router included), 7 top-k / threshold
+ * selection with compaction, 8 gather of the active rows, 9 gated scatter (with the next
+ * recursion's router logits), 10 RMSNorm; 0 turns it off.
  * At most max_launches launches are recorded (events are created here, not during calls).
  * mor_timing_read waits for the last recorded event, returns the summed kernel time in ms and
  * the number of recorded launches, and clears the record. */

@@ -49,3 +49,19 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in (r.stdout + r.stderr)
+
+
+def test_memory_kernel_bytes_at_the_360m_shape():
+    """Bytes of the memory-bound kernels of one 360M expert-choice call: the recursion-1 router
+    reads all 16,384 rows of H (63 MB), the gathers copy and the scatters read twice and write
+    once the 16,384 + 10,928 + 5,464 routed rows."""
+    cfg = workload.get_config("smol360m_bf16")
+    mb = bench.memory_kernel_bytes(cfg, _ec_counts(cfg))
+    BT, d = cfg.batch * cfg.seq, cfg.d_model
+    M = [16384, 10928, 5464]
+    assert mb["router"] == (BT * d * 4 + BT * 4, 1)
+    assert mb["gather"] == (8 * d * sum(M), 3)
+    assert mb["scatter"] == (12 * d * sum(M), 3)
+    assert mb["select"][1] == 3 and mb["select"][0] == 8 * (BT + M[0] + M[1]) + 4 * sum(M)
+    rows = 2 * 2 * BT + 2 * cfg.n_shared * sum(M)
+    assert mb["rmsnorm"] == (rows * d * 6, 2 * (2 + 3 * cfg.n_shared))
