@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.mor_prefill.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, vp, vp]
         L.mor_route.restype = i32
         L.mor_route.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
+        L.mor_route_noalloc.restype = i32
+        L.mor_route_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
         L.mor_kv_view.restype = i32
         L.mor_kv_view.argtypes = [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                   ctypes.POINTER(i32)]
@@ -104,7 +106,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("mor_abi_version", "mor_last_error", "mor_workspace_bytes", "mor_init",
-            "mor_prefill", "mor_route", "mor_kv_view", "mor_get_error_flags", "mor_timing_enable",
+            "mor_prefill", "mor_route", "mor_route_noalloc", "mor_kv_view", "mor_get_error_flags", "mor_timing_enable",
             "mor_timing_read", "mor_decode_submit", "mor_decode_continue", "mor_decode_step", "mor_decode_stats",
             "mor_destroy")
 KERNEL_KINDS = {"qkv": 1, "attention": 2, "o_proj": 3, "gate_up": 4, "down": 5, "router": 6,
@@ -303,6 +305,21 @@ class Mor:
         _check(lib().mor_route(self.handle, H.data_ptr(), active_in.data_ptr(),
                                counts_in.data_ptr(), r, B, T, act.data_ptr(), cnt.data_ptr(),
                                z.data_ptr(), _stream(stream)))
+        return act, cnt, z
+
+    def route_noalloc(self, H, active_in, counts_in, r, out=None, stream=None):
+        """mor_route_noalloc (scratch in the library's static device array): returns
+        (active_out [B, T], counts_out [B], z [B, T]); out may pass those three tensors."""
+        import torch
+        B, T, _ = H.shape
+        if out is None:
+            out = (torch.empty((B, T), dtype=torch.int32, device=H.device),
+                   torch.empty((B,), dtype=torch.int32, device=H.device),
+                   torch.empty((B, T), dtype=torch.float32, device=H.device))
+        act, cnt, z = out
+        _check(lib().mor_route_noalloc(self.handle, H.data_ptr(), active_in.data_ptr(),
+                                       counts_in.data_ptr(), r, B, T, act.data_ptr(),
+                                       cnt.data_ptr(), z.data_ptr(), _stream(stream)))
         return act, cnt, z
 
     def kv_view(self, stream_index: int):

@@ -265,6 +265,27 @@ hipError_t launch_offsets(const int* cnt, int B, int* meta, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Source row b*T + pos of every row of a compacted set (one thread per row), for callers that
+// need the row map without the gathered copy of H.
+__global__ __launch_bounds__(256) void k_rowsrc(const int* __restrict__ act, const int* __restrict__ meta,
+                                                int B, int T, int* __restrict__ rowsrc) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= meta[0]) return;
+  int lo = 0, hi = B - 1;                          // last b with meta[1+b] <= i
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (meta[1 + mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  rowsrc[i] = lo * T + act[(size_t)lo * T + (i - meta[1 + lo])];
+}
+
+hipError_t launch_rowsrc(const int* act, const int* meta, int B, int T, int m_upper, int* rowsrc,
+                         hipStream_t s) {
+  if (m_upper <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rowsrc, dim3((m_upper + 255) / 256), dim3(256), 0, s, act, meta, B, T, rowsrc);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ gather / scatter
 // One wave per compacted row i: find its sequence, copy H[src] into X[i], record the row maps
 // and the gate of the recursion update (negative gate = plain assignment).

@@ -11,6 +11,7 @@
 //   last layer on all tokens.
 // Expert-choice counts are static, so nothing is read back to the host during a call.
 #include <climits>
+#include <mutex>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -80,8 +81,19 @@ struct Cursor {
 
 }  // namespace
 
+// Scratch of mor_route_noalloc: the set's row offsets [MOR_NOALLOC_MAX_BATCH + 1] and row map
+// [MOR_NOALLOC_MAX_TOKENS]. One copy per GPU, held until the process ends; its device address is
+// looked up once per device (scratch_on) and only that address is handed to kernels.
+constexpr int kNoallocInts = MOR_NOALLOC_MAX_BATCH + 1 + MOR_NOALLOC_MAX_TOKENS;
+static __device__ __align__(256) int scratch[kNoallocInts];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static int* g_scratch_ptr[kMaxDevices] = {};
+
 struct mor_handle_s {
   mor_config cfg;
+  int device = 0;                // the GPU current at mor_init (the handle's workspace lives there)
   int n_s = 0, es = 0, nq = 0, nkv = 0, nqkv = 0, kpad = 0, nstreams = 0;
   size_t MT = 0;                 // max_batch * max_seq
   std::vector<BlockPacked> blk;  // 0 = first, 1..n_s = shared, n_s + 1 = last
@@ -645,6 +657,29 @@ mor_status copy_block(mor_handle_s* h, const mor_block_weights& src, const Block
 
 }  // namespace
 
+namespace {
+
+// Binds the static scratch of mor_route_noalloc on the current device: its device address,
+// looked up once per device with that device current.
+mor_status scratch_on(int* dev_out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOR_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOR_E_STATE, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOR_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<int*>(p);
+  }
+  *dev_out = dev;
+  return MOR_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t mor_abi_version(void) { return MOR_ABI_VERSION; }
@@ -668,9 +703,13 @@ mor_status mor_init(const mor_config* cfg, const mor_weights* w, void* workspace
   const size_t need = plan(*cfg, nullptr, nullptr);
   if (workspace_bytes < need)
     return fail(MOR_E_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " + std::to_string(need));
+  int dev = 0;
+  st = scratch_on(&dev);
+  if (st != MOR_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   auto* h = new mor_handle_s();
   h->cfg = *cfg;
+  h->device = dev;
   char* base = reinterpret_cast<char*>(((uintptr_t)workspace + kAlign - 1) / kAlign * kAlign);
   plan(*cfg, h, base);
   auto cleanup = [&](mor_status e) { delete h; return e; };
@@ -755,6 +794,36 @@ mor_status mor_route(mor_handle* h, const float* H, const int32_t* active_in,
                        nullptr, r, h->X, h->rows, h->rows + MT, h->rows + 2 * MT, h->rows + 3 * MT,
                        h->gate, s));
   HIPCHK(launch_router(H, c.d_model, h->rows + MT, meta_s, (int)BT, h->router_w + (size_t)(r - 1) * c.d_model,
+                       h->has_bias ? h->router_b + (r - 1) : nullptr, z_out, s));
+  const int k = ceil_div((long)c.cap_num[r - 1] * T, c.cap_den);
+  const int mode = c.routing == MOR_ROUTE_EC_TOPK ? SEL_EC : SEL_THRESHOLD;
+  HIPCHK(launch_select(mode, B, T, z_out, nullptr, active_in, counts_in, k, r, active_out, counts_out, h->err, s));
+  return MOR_OK;
+}
+
+mor_status mor_route_noalloc(mor_handle* h, const float* H, const int32_t* active_in,
+                             const int32_t* counts_in, int32_t r, int32_t B, int32_t T,
+                             int32_t* active_out, int32_t* counts_out, float* z_out, void* stream) {
+  if (!h || !H || !active_in || !counts_in || !active_out || !counts_out || !z_out)
+    return fail(MOR_E_INVALID, "null pointer");
+  const mor_config& c = h->cfg;
+  if (c.routing == MOR_ROUTE_TOKEN_CHOICE) return fail(MOR_E_STATE, "mor_route_noalloc: token choice not supported");
+  if (r < 1 || r > c.n_rec) return fail(MOR_E_INVALID, "r outside 1..n_rec");
+  if (B < 1 || B > c.max_batch || T < 1 || T > c.max_seq) return fail(MOR_E_SHAPE, "B or T out of range");
+  if (B > MOR_NOALLOC_MAX_BATCH || (long long)B * T > MOR_NOALLOC_MAX_TOKENS)
+    return fail(MOR_E_SHAPE, "mor_route_noalloc: B > " + std::to_string(MOR_NOALLOC_MAX_BATCH) +
+                                 " or B*T > " + std::to_string(MOR_NOALLOC_MAX_TOKENS) +
+                                 " (the static scratch holds no more); use mor_route");
+  int* sp = g_scratch_ptr[h->device];
+  if (!sp) return fail(MOR_E_STATE, "static scratch not bound on the handle's device");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int BT = B * T;
+  int* meta = sp;                                  // [B + 1]: rows, then first row of each sequence
+  int* rowsrc = sp + MOR_NOALLOC_MAX_BATCH + 1;    // [B * T]: source row of each active row
+  HIPCHK(launch_fill_f32(z_out, (size_t)BT, NAN, s));
+  HIPCHK(launch_offsets(counts_in, B, meta, s));
+  HIPCHK(launch_rowsrc(active_in, meta, B, T, BT, rowsrc, s));
+  HIPCHK(launch_router(H, c.d_model, rowsrc, meta, BT, h->router_w + (size_t)(r - 1) * c.d_model,
                        h->has_bias ? h->router_b + (r - 1) : nullptr, z_out, s));
   const int k = ceil_div((long)c.cap_num[r - 1] * T, c.cap_den);
   const int mode = c.routing == MOR_ROUTE_EC_TOPK ? SEL_EC : SEL_THRESHOLD;

@@ -63,6 +63,8 @@ hipError_t launch_select(int mode, int B, int T, const float* z, const int* dept
                          const int* act_prev, const int* cnt_prev, int k, int r, int* act_out,
                          int* cnt_out, unsigned* err, hipStream_t s);
 hipError_t launch_offsets(const int* cnt, int B, int* meta, hipStream_t s);
+hipError_t launch_rowsrc(const int* act, const int* meta, int B, int T, int m_upper, int* rowsrc,
+                         hipStream_t s);
 enum { GATE_SIGMOID = 0, GATE_ASSIGN = 1, GATE_TC = 2 };
 hipError_t launch_gather(const float* H, int d, const int* act, const int* meta, int B, int T,
                          int m_upper, int gate_kind, const float* z, const int* depth,

@@ -174,6 +174,24 @@ mor_status mor_route(mor_handle* h, const float* H, const int32_t* active_in,
                      const int32_t* counts_in, int32_t r, int32_t B, int32_t T,
                      int32_t* active_out, int32_t* counts_out, float* z_out, void* stream);
 
+/* mor_route without scratch in the workspace, for callers that cannot allocate or must not touch
+ * workspace memory another call may be using: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments, kernels and results as mor_route (router
+ * logits, selection, counts and the NaN error flag bitwise equal); the handle supplies only the
+ * router weights and the error flag. Its scratch (row offsets and the row map of the active set)
+ * is a static device array of (MOR_NOALLOC_MAX_BATCH + 1 + MOR_NOALLOC_MAX_TOKENS) int32 (about
+ * 266 KB), one per GPU, held until the process ends and bound to its device address by mor_init.
+ * The call allocates nothing. Every call on a GPU shares that GPU's array (whatever the handle),
+ * so calls that may overlap on one GPU (other streams, other threads) race: serialise them.
+ * Nothing in the array needs clearing between calls (each call writes what it reads).
+ * Errors: those of mor_route, and MOR_E_SHAPE if B > MOR_NOALLOC_MAX_BATCH or
+ * B*T > MOR_NOALLOC_MAX_TOKENS (nothing is launched then). */
+#define MOR_NOALLOC_MAX_BATCH 1024
+#define MOR_NOALLOC_MAX_TOKENS 65536
+mor_status mor_route_noalloc(mor_handle* h, const float* H, const int32_t* active_in,
+                             const int32_t* counts_in, int32_t r, int32_t B, int32_t T,
+                             int32_t* active_out, int32_t* counts_out, float* z_out, void* stream);
+
 /* Where the K/V cache of one layer stream lives after mor_prefill.
  * stream 0 = first layer, 1 + (r-1)*n_s + (j-1) = position j of recursion r, 1 + N_r*n_s = last
  * (streams 0 and 1 + N_r*n_s are not written under CYCLE / SEQUENCE sharing).

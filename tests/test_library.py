@@ -99,6 +99,7 @@ def test_null_handle_calls_rejected():
     L = mor.lib()
     assert L.mor_prefill(None, None, 1, 1, None, None, None, None, None, None) == mor.MOR_E_INVALID
     assert L.mor_route(None, None, None, None, 1, 1, 1, None, None, None, None) == mor.MOR_E_INVALID
+    assert L.mor_route_noalloc(None, None, None, None, 1, 1, 1, None, None, None, None) == mor.MOR_E_INVALID
     L.mor_destroy(None)
 
 
