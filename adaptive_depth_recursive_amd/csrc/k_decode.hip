@@ -1013,9 +1013,15 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny(const T* __restrict__ 
   const T* wrow[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) wrow[rg] = W + (size_t)(n0 + 16 * rg + fr) * K + g * MM::KW;
+  // slot rows at or past M are not loaded (their fragments stay zero and their outputs unused):
+  // with 51 of 64 rows in use that is a fifth less activation traffic per workgroup
   const T* arow[4];
+  bool arow_in[4];
 #pragma unroll
-  for (int mf = 0; mf < 4; ++mf) arow[mf] = A + (size_t)(16 * mf + fr) * K + g * MM::KW;
+  for (int mf = 0; mf < 4; ++mf) {
+    arow[mf] = A + (size_t)(16 * mf + fr) * K + g * MM::KW;
+    arow_in[mf] = 16 * mf + fr < M;
+  }
 
   for (int u0 = ulo + wave; u0 < uhi; u0 += SK_WAVES * SK_BATCH) {
     typename MM::frag wa[SK_BATCH][RG][NS], xb[SK_BATCH][4][NS];
@@ -1028,7 +1034,8 @@ __global__ __launch_bounds__(SK_WAVES * 64) void k_skinny(const T* __restrict__ 
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) wa[bt][rg][ks] = MM::load(wrow[rg] + k);
 #pragma unroll
-        for (int mf = 0; mf < 4; ++mf) xb[bt][mf][ks] = MM::load(arow[mf] + k);
+        for (int mf = 0; mf < 4; ++mf)
+          xb[bt][mf][ks] = arow_in[mf] ? MM::load(arow[mf] + k) : typename MM::frag{};
       }
     }
     // keep every load of the batch ahead of the multiplies (several loads in flight per lane)
