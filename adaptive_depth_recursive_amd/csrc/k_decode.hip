@@ -639,75 +639,74 @@ hipError_t launch_dec_output(const DecArgs& a, int fold, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ decode attention
-// One workgroup of 8 waves per (slot, KV head). It rotates the slot's new query heads and key
-// (RoPE at the token's position, fp32, then rounded to the element type), appends the new K/V to
-// the slot's page of the layer stream, and attends over the cached keys of that stream plus the
-// new one: recursion-wise caching reads the stream of the token's own recursion; recursive KV
-// sharing at r >= 2 appends nothing and reads the recursion-1 stream of the same shared layer.
-// Waves take 64-key tiles in turn. Scores: lane = key (its K row against the G query heads held
-// in LDS). Values: the tile's V rows are copied into LDS with 16-byte loads, then lane = head-dim
-// element accumulates over the tile's keys. The waves' partial results are merged in wave order.
-// Issues the loads of one 64-key tile of a slot's layer stream: lane l's K row (key t0 + l) into
-// k, and the tile's V rows into the wave's LDS tile vt ([64][HD]) with direct-to-LDS 16-byte
-// loads (instruction q, lane l: chunk 64 q + l of the tile, i.e. key (64 q + l) / chunks-per-row).
-// Keys past nkeys (>= 1) re-read key nkeys - 1: every address is a cached row. All page numbers
-// are read first (one per lane and row set, however the rows fall into pages), so the row loads
-// wait for one page-table round trip in all and then issue back to back.
-template <typename T, int HD, int KT>
-__device__ __forceinline__ void issue_dec_tile(const DecArgs& a, const T* pool, const int* pt,
-                                               size_t vofs, int kvh, int t0, int nkeys, int lane,
-                                               uint4* k, T* vt) {
-  constexpr int CH = 16 / (int)sizeof(T), RCHUNKS = HD / CH, NQ = KT * RCHUNKS / 64;
-  const int ik = min(t0 + lane, nkeys - 1);
-  int iv[NQ], pv[NQ];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) iv[q] = min(t0 + (q * 64 + lane) / RCHUNKS, nkeys - 1);
-  int pk = pt[ik / a.P];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) pv[q] = pt[iv[q] / a.P];
-  // every page number in hand before the first row load: the compiler's wait for a register
-  // loaded before a direct-to-LDS load is a full drain, which would serialise the row loads
-  pk = opaque(pk);
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) pv[q] = opaque(pv[q]);
-  const T* kr = pool + (size_t)pk * a.page_elems + ((size_t)kvh * a.P + ik % a.P) * HD;
-#pragma unroll
-  for (int c0 = 0; c0 < RCHUNKS; ++c0) k[c0] = *reinterpret_cast<const uint4*>(kr + c0 * CH);
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int cc = (q * 64 + lane) % RCHUNKS;
-    const T* vr = pool + (size_t)pv[q] * a.page_elems + vofs + ((size_t)kvh * a.P + iv[q] % a.P) * HD;
-    dma16(reinterpret_cast<const uint4*>(vr + cc * CH), reinterpret_cast<char*>(vt + q * 64 * CH));
-  }
+// One workgroup per (slot, KV head). It rotates the slot's new query heads and key (RoPE at the
+// token's position, fp32, then rounded to the element type), appends the new K/V to the slot's
+// page of the layer stream, and attends over the cached keys of that stream plus the new one:
+// recursion-wise caching reads the stream of the token's own recursion; recursive KV sharing at
+// r >= 2 appends nothing and reads the recursion-1 stream of the same shared layer.
+// A page holds one layer stream's K as [hkv][P][hd] and V transposed as [hkv][hd][P], so that
+// both operands of the products are contiguous along their reduction index: K along the head
+// dimension (scores), V^T along the keys (probabilities x values).
+// Waves take 64-key tiles in turn (wave w: keys 64 w, 64 (w + NW), ...); each keeps its own
+// running maximum, normaliser and output, and the waves' partial results (plus the new key's,
+// kept apart) are merged in a fixed order.
+//  - bf16: both products on MFMA. S^T = K Q^T with the keys as rows, read in a permuted order
+//    so that the scores a lane holds are, head by head, the 8 consecutive keys it supplies to
+//    the P V product (P as the A operand, V^T fragments straight from the page): no shuffles
+//    between the two products, no LDS for K or V.
+//  - fp32: lane = key for the scores (its K row in registers), lane = head-dim element for the
+//    values (its V^T row of the tile in registers).
+
+// Waves per (slot, KV head) workgroup: 16 for bf16 (64-key tiles on MFMA, registers for both
+// operand tiles), 8 for fp32; a context of n keys takes ceil(n / (64 NW)) tiles per wave.
+#ifndef MOR_DEC_ATTN_WAVES_BF16
+#define MOR_DEC_ATTN_WAVES_BF16 16
+#endif
+template <typename T, int HD, int G> constexpr int dec_attn_waves() {
+  return sizeof(T) == 2 ? MOR_DEC_ATTN_WAVES_BF16 : 8;
 }
 
-// Waves per (slot, KV head) workgroup: 16 where the LDS holds 16 waves' V tiles and
-// accumulators (bf16, up to 3 query heads per KV head) and the registers of 16 waves suffice
-// (head dim 64, or a single query head), else 8; a context of n keys takes ceil(n / (64 NW))
-// tiles per wave.
-template <typename T, int HD, int G> constexpr int dec_attn_waves() {
-  return sizeof(T) == 2 && G <= 3 && (HD == 64 || G == 1) ? 16 : 8;
-}
+// Page of key index k of a layer stream, and the element offset of its K row / V^T column.
+__device__ __forceinline__ int dec_page(const int* pt, int k, int P) { return pt[k / P]; }
 
 template <typename T, int HD, int G, int NW = dec_attn_waves<T, HD, G>()>
 __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j) {
   constexpr int KT = 64;
-  constexpr int CH = 16 / (int)sizeof(T);            // elements per 16-byte chunk
-  constexpr int RCHUNKS = HD / CH;                   // chunks per K/V row
+  constexpr bool MF = sizeof(T) == 2;                // bf16: MFMA tile products
+  static_assert(!MF || (HD == 64 && G <= 4), "bf16 decode attention: head dim 64, at most 4 query heads per KV head");
   __shared__ float sq[G][HD];
   __shared__ float skn[HD], svn[HD];
-  __shared__ float sp[NW][G][KT];
-  __shared__ __attribute__((aligned(16))) T sv[NW][KT * HD];
-  __shared__ float sm[NW][G], sl[NW][G];
-  __shared__ float sacc[NW][G][HD];
+  __shared__ float sp[MF ? 1 : NW][G][KT];
+  __shared__ float sm[NW + 1][G], sl[NW + 1][G];
+  __shared__ float sacc[NW + 1][G][HD];
+  // bf16: each wave's V^T tile [64 head-dim rows][64 keys], 128-byte rows with the 16-byte
+  // chunks XOR-swizzled by (row / 2) % 8 (the fragment reads of 16 consecutive rows then hit
+  // distinct bank groups)
+  __shared__ __attribute__((aligned(16))) T svt[MF ? NW : 1][MF ? KT * HD : 1];
 
   touch_args(a);
   const int s = blockIdx.x, kvh = blockIdx.y;       // the grid has one row per slot
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // The slot's state in one round trip: flag, position, depth and every per-recursion count (the
-  // count this layer needs depends on the depth). The empty asm uses every value before the
-  // participation test, so the compiler cannot move the other loads behind it.
+  const int P = a.P;
+  // The page numbers of this wave's first tile (keys 64 w .. 64 w + 63, at most 4 pages) are
+  // read before the slot's depth is known, for every layer stream the depth could select (the
+  // unique layer's stream, or recursion c + 1's stream of shared position j): lane 4 c + i
+  // holds page i of candidate c. Entries past a stream's allocated pages are still valid page
+  // numbers (the table is cleared at init and only ever holds page numbers), and the keys they
+  // would serve are masked.
+  const int ncand = kind == DL_SHARED ? a.R : 1;
+  int spec_pg = 0;
+  {
+    const int c = lane >> 2, i = lane & 3;
+    if (c < ncand) {
+      const int ls = kind == DL_FIRST ? 0 : kind == DL_LAST ? 1 : layer_stream_shared(a, c + 1, j);
+      spec_pg = a.ptab[((size_t)s * a.LS + ls) * a.pps + min(wave * KT / P + i, a.pps - 1)];
+    }
+  }
+  // The slot's state in the same round trip: flag, position, depth and every per-recursion
+  // count (the count this layer needs depends on the depth). The empty asm uses every value
+  // before the participation test, so the compiler cannot move the other loads behind it.
   const int* flag = kind == DL_FIRST ? a.sl_first : kind == DL_LAST ? a.sl_exit : a.sl_part;
   const int part = flag[s];
   const int sbase = a.sl_base[s], spos = a.sl_pos[s], r = a.sl_depth[s];
@@ -717,6 +716,7 @@ __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j
   use_now(part); use_now(sbase); use_now(spos); use_now(r);
 #pragma unroll
   for (int q = 0; q < MOR_MAX_REC_DEV; ++q) use_now(cnt[q]);
+  asm volatile("" ::"v"(spec_pg));
   // the arguments used before the first barrier, so their loads share the first round trip
   use_now(a.n_s); use_now(a.P); use_now(a.pps); use_now(a.LS); use_now(a.nqkv); use_now(a.kv_share);
   use_now(a.page_elems); use_now(a.ptab); use_now(a.pool); use_now(a.qkv); use_now(a.rope_cos);
@@ -743,135 +743,311 @@ __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j
     nkeys = c;
   }
   T* pool = reinterpret_cast<T*>(a.pool);
-  const size_t vofs = (size_t)a.hkv * a.P * HD;
+  const size_t vofs = (size_t)a.hkv * P * HD;        // V^T part of a page
+  // candidate of the stream read here: recursion r's (shared, recursion-wise), recursion 1's
+  // (shared under KV sharing), the unique layer's
+  const int csel = (kind == DL_SHARED && !(a.kv_share && r >= 2)) ? r - 1 : 0;
   const int* pt = a.ptab + ((size_t)s * a.LS + ls_r) * a.pps;
   // page of the appended key and value, read early by the threads that store them (a per-thread
   // value, so nothing waits for it before the barrier)
-  const int page_w = (ls_w >= 0 && tid < 2 * HD) ? a.ptab[((size_t)s * a.LS + ls_w) * a.pps + idx_w / a.P] : 0;
-  T* svw = sv[wave];
+  const int page_w = (ls_w >= 0 && tid < 2 * HD) ? a.ptab[((size_t)s * a.LS + ls_w) * a.pps + idx_w / P] : 0;
+  const int fr = lane & 15, g = lane >> 4;
+
   // This wave's first tile is issued before the query/key/value fold below, so its page-table
-  // and row loads overlap the fold's: K rows into registers (lane = key), V rows into the
-  // wave's LDS tile by direct-to-LDS loads.
+  // and row loads overlap the fold's.
+  //  bf16: K fragments kf[kb][ks] into registers (A operand of S^T: row fr of key block kb is
+  //  the key t0 + 32 (kb / 2) + 8 (fr / 4) + 4 (kb % 2) + fr % 4, head-dim elements
+  //  32 ks + 8 g ..+7), and the V^T tile into the wave's LDS tile by direct-to-LDS loads
+  //  (instruction q, lane l: LDS chunk 64 q + l = row (64 q + l) / 8, physical chunk l % 8,
+  //  i.e. keys 8 ((l % 8) ^ swizzle(row)) ..+7 of that head-dim row). Keys past the context
+  //  read the last cached key (valid memory; an 8-key group never crosses a page: P is a
+  //  multiple of 8); their scores are masked (zero probabilities).
+  //  fp32: lane = key: its K row; lane = head-dim element: its V^T row of the tile.
   int t0 = wave * KT;
-  union KRow { uint4 u[RCHUNKS]; T e[RCHUNKS * CH]; } kc;
-  if (t0 < nkeys) issue_dec_tile<T, HD, KT>(a, pool, pt, vofs, kvh, t0, nkeys, lane, kc.u, svw);
+  const bool lane_c = lane < HD;
+  bf16x8 kf[MF ? 4 : 1][2];
+  constexpr int KCH = MF ? 1 : HD / 4;               // fp32: 16-byte chunks of a K row
+  float4 kr32[KCH], vr32[MF ? 1 : KT / 4];
+  // page of key k of tile tt: on the wave's first tile from the speculative reads (a lane
+  // exchange), on later tiles from the page table
+  auto page_of = [&](int tt, int k, bool first) -> int {
+    return first ? __shfl(spec_pg, 4 * csel + (k / P - tt / P)) : dec_page(pt, k, P);
+  };
+  auto issue_tile = [&](int tt, bool first) {
+    if constexpr (MF) {
+      // every page number in hand before the first row load (the compiler's wait for a
+      // register loaded before a direct-to-LDS load is a full drain, which would serialise them)
+      int kpg[4], vpg[8];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int key = min(tt + 32 * (kb >> 1) + 8 * (fr >> 2) + 4 * (kb & 1) + (fr & 3), nkeys - 1);
+        kpg[kb] = opaque(page_of(tt, key, first));
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int row = (64 * q + lane) >> 3;
+        const int key = min(tt + 8 * ((lane & 7) ^ ((row >> 1) & 7)), (nkeys - 1) & ~7);
+        vpg[q] = opaque(page_of(tt, key, first));
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int key = min(tt + 32 * (kb >> 1) + 8 * (fr >> 2) + 4 * (kb & 1) + (fr & 3), nkeys - 1);
+        const T* kp = pool + (size_t)kpg[kb] * a.page_elems + ((size_t)kvh * P + key % P) * HD;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) kf[kb][ks] = *reinterpret_cast<const bf16x8*>(kp + 32 * ks + 8 * g);
+      }
+      char* dst = reinterpret_cast<char*>(svt[wave]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int row = (64 * q + lane) >> 3;
+        const int key = min(tt + 8 * ((lane & 7) ^ ((row >> 1) & 7)), (nkeys - 1) & ~7);
+        const T* vp = pool + (size_t)vpg[q] * a.page_elems + vofs + ((size_t)kvh * HD + row) * P + key % P;
+        dma16(reinterpret_cast<const uint4*>(vp), dst + q * 1024);
+      }
+    } else {
+      const int key = min(tt + lane, nkeys - 1);
+      const T* kp = pool + (size_t)page_of(tt, key, first) * a.page_elems + ((size_t)kvh * P + key % P) * HD;
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) kr32[c] = *reinterpret_cast<const float4*>(kp + 4 * c);
+#pragma unroll
+      for (int q = 0; q < KT / 4; ++q) {
+        const int k4 = min(tt + 4 * q, (nkeys - 1) & ~3);
+        const int pg = page_of(tt, k4, first);      // a lane exchange: every lane takes part
+        if (lane_c) {
+          const T* vp = pool + (size_t)pg * a.page_elems + vofs + ((size_t)kvh * HD + lane) * P + k4 % P;
+          vr32[q] = *reinterpret_cast<const float4*>(vp);
+        }
+      }
+    }
+  };
   // Query heads, key and value of the slot's token: the K-split partial sums added in split
-  // order, RoPE on q and k, rounded to the element type. Every load of a thread (both halves'
-  // partial sums and the rotation) is issued before any of them is used.
+  // order, RoPE on q and k, rounded to the element type. Thread i < (G + 2) HD owns element i
+  // (the grid has at least that many threads): its loads (both halves' partial sums and the
+  // rotation) are issued first, then this wave's first K/V tile, then the fold, which therefore
+  // waits only for its own loads.
+  static_assert(NW * 64 >= (G + 2) * HD, "one fold element per thread");
   const int half = HD / 2;
-  const float* qkv = a.qkv + (size_t)s * a.nqkv;
-  for (int i = tid; i < (G + 2) * HD; i += NW * 64) {
-    const int hh = i / HD, c = i % HD;
-    const int pc = c < half ? c + half : c - half;
-    const float* base;
-    if (hh < G) base = qkv + (kvh * G + hh) * HD;
-    else if (hh == G) base = qkv + a.nq + kvh * HD;
-    else base = qkv + a.nq + a.nkv + kvh * HD;
-    const size_t split = (size_t)64 * a.nqkv;     // partial sums of the K splits, added in order
-    const int f = c % half;
-    const float cs = a.rope_cos[pos * half + f], sn = a.rope_sin[pos * half + f];
-    const float v0 = fold_splits(base[c], base + split + c, split, a.kqkv - 1);
-    const float vp = fold_splits(base[pc], base + split + pc, split, a.kqkv - 1);
-    const float rot = c < half ? v0 * cs - vp * sn : v0 * cs + vp * sn;
-    const float v = to_f32(from_f32<T>(hh <= G ? rot : v0));
-    if (hh < G) sq[hh][c] = v;
-    else if (hh == G) skn[c] = v;
-    else svn[c] = v;
+  const bool fold_on = tid < (G + 2) * HD;
+  const int fh = tid / HD, fc = tid % HD;
+  const int fpc = fc < half ? fc + half : fc - half;
+  float f0[kMaxQkvSplits], f1[kMaxQkvSplits], fcs = 0.f, fsn = 0.f;
+  {
+    const float* qkv = a.qkv + (size_t)s * a.nqkv;
+    const float* base = fh < G ? qkv + (kvh * G + min(fh, G - 1)) * HD
+                        : fh == G ? qkv + a.nq + kvh * HD : qkv + a.nq + a.nkv + kvh * HD;
+    const size_t split = (size_t)64 * a.nqkv;       // partial sums of the K splits
+    const int nsp = a.kqkv;
+    if (fold_on) {
+      const int f = fc % half;
+      fcs = a.rope_cos[pos * half + f];
+      fsn = a.rope_sin[pos * half + f];
+#pragma unroll
+      for (int q = 0; q < kMaxQkvSplits; ++q) {     // splits past nsp re-read split 0 (unused)
+        f0[q] = base[(q < nsp ? q : 0) * split + fc];
+        f1[q] = base[(q < nsp ? q : 0) * split + fpc];
+      }
+    }
+  }
+  if (t0 < nkeys) issue_tile(t0, true);
+  if (fold_on) {
+    float v0 = f0[0], vp = f1[0];
+#pragma unroll
+    for (int q = 1; q < kMaxQkvSplits; ++q)
+      if (q < a.kqkv) { v0 = v0 + f0[q]; vp = vp + f1[q]; }
+    const float rot = fc < half ? v0 * fcs - vp * fsn : v0 * fcs + vp * fsn;
+    const float v = to_f32(from_f32<T>(fh <= G ? rot : v0));
+    if (fh < G) sq[fh][fc] = v;
+    else if (fh == G) skn[fc] = v;
+    else svn[fc] = v;
   }
   __syncthreads();
   if (ls_w >= 0 && tid < 2 * HD) {
     const int pw = opaque(page_w);     // keeps the address arithmetic (and its wait) after the barrier
-    T* dst = pool + (size_t)pw * a.page_elems + ((size_t)kvh * a.P + idx_w % a.P) * HD;
-    if (tid < HD) dst[tid] = from_f32<T>(skn[tid]);
-    else dst[vofs + tid - HD] = from_f32<T>(svn[tid - HD]);
+    T* dst = pool + (size_t)pw * a.page_elems;
+    if (tid < HD) dst[((size_t)kvh * P + idx_w % P) * HD + tid] = from_f32<T>(skn[tid]);
+    else dst[vofs + ((size_t)kvh * HD + (tid - HD)) * P + idx_w % P] = from_f32<T>(svn[tid - HD]);
   }
 
   const float sl2 = a.scale_log2;
-  float m[G], l[G], acc[G];
-  const bool lane_c = lane < HD;
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) { m[hh] = -INFINITY; l[hh] = 0.f; acc[hh] = 0.f; }
-  if (wave == 0 && ls_w >= 0) {            // the new key: p = exp2(0) = 1
+  // The new key: p = exp2(0) = 1 against its own score; a partial result of its own.
+  if (wave == 0 && ls_w >= 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       // lane c forms q[c] k[c], the wave sums them (a shuffle tree, not a 64-long chain)
       const float dot = wave_sum(lane_c ? sq[hh][lane] * skn[lane] : 0.f);
-      m[hh] = dot * sl2;
-      l[hh] = 1.f;
-      acc[hh] = lane_c ? svn[lane] : 0.f;
+      if (lane == 0) { sm[NW][hh] = dot * sl2; sl[NW][hh] = 1.f; }
+      if (lane_c) sacc[NW][hh][lane] = svn[lane];
     }
   }
-  for (; t0 < nkeys; t0 += NW * KT) {
-    const int nt = min(KT, nkeys - t0);
-    const int i = t0 + lane;
-    const bool valid = i < nkeys;
-    float sc[G];
+
+  if constexpr (MF) {
+    // query fragments (B operand of S^T): head fr (zero past G), head-dim elements 32 ks + 8 g ..+7
+    bf16x8 qb[2];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) sc[hh] = 0.f;
-    if (valid) {
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int e = 0; e < RCHUNKS * CH; ++e) {
-        const float kv = to_f32(kc.e[e]);
+      for (int e = 0; e < 8; ++e) qb[ks][e] = (bf16)(fr < G ? sq[fr < G ? fr : 0][32 * ks + 8 * g + e] : 0.f);
+    // this lane's head is fr (its scores, maximum and normaliser); its output rows are the heads
+    // 4 g + e (only g = 0 holds heads, G <= 4), head-dim columns 16 hb + fr
+    float m = -INFINITY, l = 0.f;
+    f32x4 o[4];
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) sc[hh] += sq[hh][e] * kv;
+    for (int hb = 0; hb < 4; ++hb) o[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool head_ok = fr < G;
+    for (; t0 < nkeys; t0 += NW * KT) {
+      f32x4 st[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][0], qb[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][1], qb[1], st[kb], 0, 0, 0);
       }
+      // st[kb][e]: score of key t0 + 32 (kb / 2) + 8 g + 4 (kb % 2) + e for head fr
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = t0 + 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + e;
+          st[kb][e] = key < nkeys ? st[kb][e] * sl2 : -INFINITY;
+          mx = fmaxf(mx, st[kb][e]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);                // the tile holds at least one key: finite
+      const float alpha = exp2f(m - mn);            // 0 on the first tile (m = -inf)
+      m = mn;
+      l *= alpha;
+      // rescale the output rows: head e's factor lives in lane e
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ae = __shfl(alpha, e);
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) o[hb][e] *= ae;
+      }
+      bf16x8 pf[2];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pv = head_ok ? exp2f(st[kb][e] - mn) : 0.f;
+          l += pv;
+          pf[kb >> 1][4 * (kb & 1) + e] = (bf16)pv;
+        }
+      // the tile's V^T rows have landed in the wave's LDS tile (direct-to-LDS loads count as
+      // vector memory loads)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // V^T fragments (B operand of P V: head-dim column 16 hb + fr, keys t0 + 32 ks + 8 g ..+7).
+      // Keys past the context have zero probabilities; their page slots hold zeros or values an
+      // earlier request stored (the pool is cleared at init), so every product term is finite.
+      const char* vt = reinterpret_cast<const char*>(svt[wave]);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 vv[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+          const int row = 16 * hb + fr;
+          vv[hb] = *reinterpret_cast<const bf16x8*>(vt + row * 128 + (((4 * ks + g) ^ ((row >> 1) & 7)) << 4));
+        }
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          o[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ks], vv[hb], o[hb], 0, 0, 0);
+      }
+      if (t0 + NW * KT < nkeys) {
+        // the next tile's V^T overwrites this one: every fragment read of it has completed
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        issue_tile(t0 + NW * KT, false);
+      }
+    }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (g == 0 && head_ok) { sm[wave][fr] = m; sl[wave][fr] = l; }
+    if (g == 0) {
+#pragma unroll
+      for (int e = 0; e < G; ++e)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) sacc[wave][e][16 * hb + fr] = o[hb][e];
+    }
+  } else {
+    float m[G], l[G], acc[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) { m[hh] = -INFINITY; l[hh] = 0.f; acc[hh] = 0.f; }
+    for (; t0 < nkeys; t0 += NW * KT) {
+      const int nt = min(KT, nkeys - t0);
+      const bool valid = t0 + lane < nkeys;
+      float sc[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) sc[hh] = 0.f;
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) {
+        const float4 kv = kr32[c];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+          sc[hh] += sq[hh][4 * c] * kv.x + sq[hh][4 * c + 1] * kv.y + sq[hh][4 * c + 2] * kv.z + sq[hh][4 * c + 3] * kv.w;
+      }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float v = valid ? sc[hh] * sl2 : -INFINITY;
+        float mt = v;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o));
+        const float mn = fmaxf(m[hh], mt);
+        const float alpha = exp2f(m[hh] - mn);
+        const float p = valid ? exp2f(v - mn) : 0.f;
+        l[hh] = l[hh] * alpha + wave_sum(p);
+        acc[hh] *= alpha;
+        m[hh] = mn;
+        sp[wave][hh][lane] = p;
+      }
+      // this wave's probabilities are read back by the other lanes of the wave
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (lane_c) {
+#pragma unroll
+        for (int q = 0; q < KT / 4; ++q) {
+          const float4 vv = vr32[q];
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            if (4 * q + 0 < nt) acc[hh] += sp[wave][hh][4 * q + 0] * vv.x;
+            if (4 * q + 1 < nt) acc[hh] += sp[wave][hh][4 * q + 1] * vv.y;
+            if (4 * q + 2 < nt) acc[hh] += sp[wave][hh][4 * q + 2] * vv.z;
+            if (4 * q + 3 < nt) acc[hh] += sp[wave][hh][4 * q + 3] * vv.w;
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (t0 + NW * KT < nkeys) issue_tile(t0 + NW * KT, false);
     }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float v = valid ? sc[hh] * sl2 : -INFINITY;
-      float mt = v;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o));
-      const float mn = fmaxf(m[hh], mt);
-      const float alpha = exp2f(m[hh] - mn);
-      const float p = valid ? exp2f(v - mn) : 0.f;
-      l[hh] = l[hh] * alpha + wave_sum(p);
-      acc[hh] *= alpha;
-      m[hh] = mn;
-      sp[wave][hh][lane] = to_f32(from_f32<T>(p));
+      if (lane == 0) { sm[wave][hh] = m[hh]; sl[wave][hh] = l[hh]; }
+      if (lane_c) sacc[wave][hh][lane] = acc[hh];
     }
-    // this wave's LDS writes (probabilities, V rows) are read back by other lanes of the wave
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // the tile's V rows have landed in LDS (direct-to-LDS loads count as vector memory loads)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (lane_c) {
-#pragma unroll 8
-      for (int kk = 0; kk < nt; ++kk) {
-        const float vv = to_f32(svw[kk * HD + lane]);
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) acc[hh] += sp[wave][hh][kk] * vv;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // the next tile of this wave (its V tile overwrites the one just read)
-    if (t0 + NW * KT < nkeys) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      issue_dec_tile<T, HD, KT>(a, pool, pt, vofs, kvh, t0 + NW * KT, nkeys, lane, kc.u, svw);
-    }
-  }
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    if (lane == 0) { sm[wave][hh] = m[hh]; sl[wave][hh] = l[hh]; }
-    if (lane_c) sacc[wave][hh][lane] = acc[hh];
   }
   __syncthreads();
-  // Wave hh merges query head hh, in wave order, over the waves that held keys (wave 0 and the
-  // waves with a tile; the others hold m = -inf, l = 0, acc = 0 and would add exact zeros).
-  const int nw_used = min(NW, max(1, (nkeys + KT - 1) / KT));
+  // Wave hh merges query head hh: the waves that held keys in wave order, then the new key.
+  const int nw_used = min(NW, (nkeys + KT - 1) / KT);
   if (wave < G && lane_c) {
     const int hh = wave;
     T* out = reinterpret_cast<T*>(a.o) + (size_t)s * a.nq;
+    const bool with_new = ls_w >= 0;
     float M = -INFINITY;
     for (int w = 0; w < nw_used; ++w) M = fmaxf(M, sm[w][hh]);
+    if (with_new) M = fmaxf(M, sm[NW][hh]);
     float L = 0.f, o = 0.f;
     for (int w = 0; w < nw_used; ++w) {
-      const float f = (sm[w][hh] == -INFINITY) ? 0.f : exp2f(sm[w][hh] - M);
+      const float f = exp2f(sm[w][hh] - M);
       L += sl[w][hh] * f;
       o += sacc[w][hh][lane] * f;
+    }
+    if (with_new) {
+      const float f = exp2f(sm[NW][hh] - M);
+      L += sl[NW][hh] * f;
+      o += sacc[NW][hh][lane] * f;
     }
     out[(kvh * G + hh) * HD + lane] = from_f32<T>(o / L);
   }
@@ -892,11 +1068,15 @@ static hipError_t dec_attn_g(const DecArgs& a, int kind, int j, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_dec_attn(const DecArgs& a, int kind, int j, hipStream_t s) {
-  switch (a.hd) {
-    case 16: return dec_attn_g<T, 16>(a, kind, j, s);
-    case 32: return dec_attn_g<T, 32>(a, kind, j, s);
-    case 64: return dec_attn_g<T, 64>(a, kind, j, s);
-    default: return hipErrorInvalidValue;
+  if constexpr (sizeof(T) == 2) {      // bf16 configurations have head dim 64
+    return a.hd == 64 ? dec_attn_g<T, 64>(a, kind, j, s) : hipErrorInvalidValue;
+  } else {
+    switch (a.hd) {
+      case 16: return dec_attn_g<T, 16>(a, kind, j, s);
+      case 32: return dec_attn_g<T, 32>(a, kind, j, s);
+      case 64: return dec_attn_g<T, 64>(a, kind, j, s);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 template hipError_t launch_dec_attn<float>(const DecArgs&, int, int, hipStream_t);
@@ -964,8 +1144,9 @@ __global__ void k_dec_prefix_copy(DecArgs a, PrefixSrc p, int nstreams) {
   const T v = isv ? vt[(((size_t)b * a.hkv + h) * HDk + c) * p.kpad + idx]
                   : k[((size_t)b * p.kpad + idx) * row + h * HDk + c];
   const int page = a.ptab[((size_t)b * a.LS + ls) * a.pps + idx / a.P];
-  T* dst = reinterpret_cast<T*>(a.pool) + (size_t)page * a.page_elems + (isv ? (size_t)a.hkv * a.P * HDk : 0) +
-           ((size_t)h * a.P + idx % a.P) * HDk + c;
+  T* dst = reinterpret_cast<T*>(a.pool) + (size_t)page * a.page_elems +
+           (isv ? (size_t)a.hkv * a.P * HDk + ((size_t)h * HDk + c) * a.P + idx % a.P
+                : ((size_t)h * a.P + idx % a.P) * HDk + c);
   *dst = v;
 }
 

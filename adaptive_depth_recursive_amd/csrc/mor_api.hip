@@ -64,7 +64,7 @@ constexpr size_t kAlign = 256;
 #endif
 constexpr int kSplitQKV = MOR_DEC_SPLIT_QKV, kSplitO = MOR_DEC_SPLIT_O, kSplitDown = MOR_DEC_SPLIT_DOWN;
 constexpr int kSplitPx = kSplitO > kSplitDown ? kSplitO : kSplitDown;
-static_assert(kSplitQKV >= 1 && kSplitQKV <= 8, "QKV split out of range");
+static_assert(kSplitQKV >= 1 && kSplitQKV <= kMaxQkvSplits, "QKV split out of range");
 static_assert(kSplitO >= 1 && kSplitO <= 8 && kSplitDown >= 1 && kSplitDown <= 8, "split out of range");
 
 struct Cursor {
@@ -751,6 +751,12 @@ mor_status mor_init(const mor_config* cfg, const mor_weights* w, void* workspace
     if (e == hipSuccess) e = hipMemsetAsync(h->dHf, 0, 64 * (size_t)cfg->d_ff * h->es, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->dec.glob, 0, G_COUNT * 4, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->dec.sl_req, 0xFF, cfg->max_slots * 4, s);
+    // every page slot holds a finite value before its first write (decode attention multiplies
+    // the values of a tile's unused key slots by zero probabilities), and every page-table
+    // entry a valid page
+    if (e == hipSuccess) e = hipMemsetAsync(h->dec.pool, 0, (size_t)h->kv_pages * h->page_bytes, s);
+    if (e == hipSuccess)
+      e = hipMemsetAsync(h->dec.ptab, 0, (size_t)cfg->max_slots * h->LS * h->pps * sizeof(int), s);
   }
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {

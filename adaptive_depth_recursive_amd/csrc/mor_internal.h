@@ -95,6 +95,9 @@ enum { DL_FIRST = 0, DL_SHARED = 1, DL_LAST = 2 };
 
 // Everything the decode kernels read or write. Slots are the rows of every decode GEMM (at most
 // 64, padded to 64 rows); a slot holds one request, and at most one of its tokens is in flight.
+// K splits of the decode QKV projection that decode attention folds (at most).
+constexpr int kMaxQkvSplits = 4;
+
 struct DecArgs {
   int S, R, n_s, P, pps, LS;           // slots, N_r, shared layers, page tokens, pages per stream, layer streams
   int d, hd, hkv, hq, nq, nkv, nqkv;
