@@ -71,6 +71,12 @@ __device__ __forceinline__ void touch_args(const DecArgs& a) {
 __device__ __forceinline__ void dma16(const uint4* src, char* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
 }
+// The same with the non-temporal (streaming) cache policy, for K/V page reads: an iteration
+// reads tens of MB of pages once each, which would otherwise push the layer weights (read every
+// iteration) out of the caches.
+__device__ __forceinline__ void dma16_nt(const uint4* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 2 /* nt */);
+}
 
 }  // namespace
 
@@ -755,6 +761,7 @@ __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j
 
   // This wave's first tile is issued before the query/key/value fold below, so its page-table
   // and row loads overlap the fold's.
+  //  K/V page reads use the non-temporal cache policy (see dma16_nt).
   //  bf16: K fragments kf[kb][ks] into registers (A operand of S^T: row fr of key block kb is
   //  the key t0 + 32 (kb / 2) + 8 (fr / 4) + 4 (kb % 2) + fr % 4, head-dim elements
   //  32 ks + 8 g ..+7), and the V^T tile into the wave's LDS tile by direct-to-LDS loads
@@ -794,7 +801,8 @@ __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j
         const int key = min(tt + 32 * (kb >> 1) + 8 * (fr >> 2) + 4 * (kb & 1) + (fr & 3), nkeys - 1);
         const T* kp = pool + (size_t)kpg[kb] * a.page_elems + ((size_t)kvh * P + key % P) * HD;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) kf[kb][ks] = *reinterpret_cast<const bf16x8*>(kp + 32 * ks + 8 * g);
+        for (int ks = 0; ks < 2; ++ks)
+          kf[kb][ks] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(kp + 32 * ks + 8 * g));
       }
       char* dst = reinterpret_cast<char*>(svt[wave]);
 #pragma unroll
@@ -802,20 +810,24 @@ __global__ __launch_bounds__(NW * 64) void k_dec_attn(DecArgs a, int kind, int j
         const int row = (64 * q + lane) >> 3;
         const int key = min(tt + 8 * ((lane & 7) ^ ((row >> 1) & 7)), (nkeys - 1) & ~7);
         const T* vp = pool + (size_t)vpg[q] * a.page_elems + vofs + ((size_t)kvh * HD + row) * P + key % P;
-        dma16(reinterpret_cast<const uint4*>(vp), dst + q * 1024);
+        dma16_nt(reinterpret_cast<const uint4*>(vp), dst + q * 1024);
       }
     } else {
       const int key = min(tt + lane, nkeys - 1);
       const T* kp = pool + (size_t)page_of(tt, key, first) * a.page_elems + ((size_t)kvh * P + key % P) * HD;
 #pragma unroll
-      for (int c = 0; c < KCH; ++c) kr32[c] = *reinterpret_cast<const float4*>(kp + 4 * c);
+      for (int c = 0; c < KCH; ++c) {
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kp + 4 * c));
+        kr32[c] = make_float4(v[0], v[1], v[2], v[3]);
+      }
 #pragma unroll
       for (int q = 0; q < KT / 4; ++q) {
         const int k4 = min(tt + 4 * q, (nkeys - 1) & ~3);
         const int pg = page_of(tt, k4, first);      // a lane exchange: every lane takes part
         if (lane_c) {
           const T* vp = pool + (size_t)pg * a.page_elems + vofs + ((size_t)kvh * HD + lane) * P + k4 % P;
-          vr32[q] = *reinterpret_cast<const float4*>(vp);
+          const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(vp));
+          vr32[q] = make_float4(v[0], v[1], v[2], v[3]);
         }
       }
     }
