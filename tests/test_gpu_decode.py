@@ -281,6 +281,39 @@ def test_decode_long_context_bf16():
     model.close()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_128_token_pages(dtype):
+    """Pages of 128 tokens (larger than a 64-key attention tile: a tile reads half a page) with a
+    request that fills several pages; bf16 teacher-forced, fp32 free-running."""
+    cfg = workload.get_config("small_thr_bf16", dtype=dtype, max_len=512)
+    model, W, lens = _setup(cfg, slots=3, page=128, lengths=[300, 129, 17])
+    inputs = workload.make_decode_inputs(cfg, lens)
+    res = _run(model, cfg, lens, inputs)
+    _check_routing(cfg, W, res, lens)
+    worst = _compare(cfg, W, res, lens, inputs, teacher=dtype == "bf16")
+    say(f"[gpu] decode {dtype} 128-token pages: worst rel err {worst:.2e}")
+    model.close()
+
+
+def test_decode_full_size_kv_share_sampled():
+    """The 360M MoR-4 workload with recursive KV sharing at its launch configuration (51 slots,
+    64-token pages): the first 60 requests, routing stage-wise on every token, the longest and
+    the shortest request against the oracle (teacher-forced)."""
+    cfg = workload.get_config("smol360m_mor4_decode", kv_mode="share")
+    bias = np.array(_gold("decode_router_bias.json")["router_b"], np.float32)
+    lens = workload.make_decode_lengths(cfg)[:60]
+    model, W, lens = _setup(cfg, slots=cfg.slots, bias=bias, page=64, lengths=lens)
+    inputs = workload.make_decode_inputs(cfg, lens)
+    res = _run(model, cfg, lens, inputs)
+    _check_routing(cfg, W, res, lens)
+    order = np.argsort(lens, kind="stable")
+    which = [int(order[-1]), int(order[0])]
+    say(f"[cpu] oracle on requests {which} (lengths {lens[which].tolist()})")
+    worst = _compare(cfg, W, res, lens, inputs, teacher=True, which=set(which))
+    say(f"[gpu] full-size KV-sharing decode: {int(lens.sum())} tokens, worst rel err {worst:.2e}")
+    model.close()
+
+
 def test_decode_long_context_f32_free_running():
     """fp32 decode attention runs 8 waves (512 keys per round): a 700-token request crosses into
     the second round in the first and last layers and in the recursion-1 layers. Free-running:
