@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.mor_timing_enable.argtypes = [vp, i32, i32]
         L.mor_timing_read.restype = i32
         L.mor_timing_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
+        L.mor_timing_clock.restype = i32
+        L.mor_timing_clock.argtypes = [vp, ctypes.POINTER(ctypes.c_double)]
         L.mor_decode_submit.restype = i32
         L.mor_decode_submit.argtypes = [vp, i32, ctypes.POINTER(i32), vp, vp, vp, vp, vp, vp]
         L.mor_decode_continue.restype = i32
@@ -107,7 +109,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("mor_abi_version", "mor_last_error", "mor_workspace_bytes", "mor_init",
             "mor_prefill", "mor_route", "mor_route_noalloc", "mor_kv_view", "mor_get_error_flags", "mor_timing_enable",
-            "mor_timing_read", "mor_decode_submit", "mor_decode_continue", "mor_decode_step", "mor_decode_stats",
+            "mor_timing_read", "mor_timing_clock", "mor_decode_submit", "mor_decode_continue", "mor_decode_step", "mor_decode_stats",
             "mor_destroy")
 KERNEL_KINDS = {"qkv": 1, "attention": 2, "o_proj": 3, "gate_up": 4, "down": 5, "router": 6,
                 "select": 7, "gather": 8, "scatter": 9, "rmsnorm": 10}
@@ -403,6 +405,13 @@ class Mor:
         ms, n = ctypes.c_double(), ctypes.c_int32()
         _check(lib().mor_timing_read(self.handle, ctypes.byref(ms), ctypes.byref(n)))
         return ms.value, n.value
+
+    def timing_clock(self) -> float:
+        """Shader clock in GHz over the projection launches recorded since timing_enable (0.0 if
+        none were sampled)."""
+        ghz = ctypes.c_double()
+        _check(lib().mor_timing_clock(self.handle, ctypes.byref(ghz)))
+        return ghz.value
 
     def error_flags(self, stream=None) -> int:
         f = ctypes.c_uint32()

@@ -95,6 +95,11 @@ __global__ __launch_bounds__(128 * NWM, (NWM == 4 && BN * BM <= 128 * 192) ? 2 :
   int m0 = 0, n0 = 0;
   int t = next_tile(tbase + slot, m0, n0);
   if (t < 0) return;
+  // clock sampling (measurement hook): the first workgroup, which always holds tile 0, reads the
+  // shader cycle counter and the constant-rate real-time counter at its start and end
+  const bool sample_clk = ep.clk != nullptr && bid == 0;
+  long long clk_c0 = 0, clk_r0 = 0;
+  if (sample_clk) { clk_c0 = clock64(); clk_r0 = wall_clock64(); }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave / NWM, wm = wave % NWM;
@@ -286,6 +291,10 @@ __global__ __launch_bounds__(128 * NWM, (NWM == 4 && BN * BM <= 128 * 192) ? 2 :
     if (tnext < 0) break;
     t = tnext; m0 = nm0; n0 = nn0;
     buf0 = (buf0 + nk) & 1;
+  }
+  if (sample_clk && threadIdx.x == 0) {
+    atomicAdd(ep.clk, (unsigned long long)(clock64() - clk_c0));
+    atomicAdd(ep.clk + 1, (unsigned long long)(wall_clock64() - clk_r0));
   }
 }
 

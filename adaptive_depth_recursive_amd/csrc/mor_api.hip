@@ -122,6 +122,7 @@ struct mor_handle_s {
   int* rows = nullptr;           // 4 x [MT]: the same for the current active set
   float* gate = nullptr;         // [MT]
   unsigned* err = nullptr;
+  unsigned long long* clk = nullptr;  // [2] shader cycles / real-time ticks of the timed projection kind
   // depth-wise batched decode
   bool decode = false;
   int kv_pages = 0, pps = 0, LS = 0;
@@ -256,6 +257,7 @@ size_t plan(const mor_config& c, mor_handle_s* h, char* base) {
   int* rows = cur.take<int>(4 * MT * 4);
   float* gate = cur.take<float>(MT * 4);
   unsigned* err = cur.take<unsigned>(64);
+  unsigned long long* clk = cur.take<unsigned long long>(2 * 8);
   // decode engine
   const int S = c.max_slots;
   const int P = S ? c.kv_page_tokens : 1;
@@ -301,6 +303,7 @@ size_t plan(const mor_config& c, mor_handle_s* h, char* base) {
     h->act = act; h->cnt = cnt; h->meta = meta; h->z = z; h->tc_logits = tc_logits;
     h->depth = depth; h->prob = prob; h->rows_all = rows_all; h->rows = rows; h->gate = gate;
     h->err = err;
+    h->clk = clk;
     h->decode = S > 0;
     if (S) {
       h->kv_pages = kv_pages; h->pps = pps; h->LS = LS; h->page_bytes = page_bytes;
@@ -390,6 +393,7 @@ mor_status run_layer(mor_handle_s* h, const BlockPacked& w, float* X, const RowS
   const int n_qkv = k_dst ? h->nqkv : h->nq;
   {
     TimedLaunch t(h, KIND_QKV, s);
+    ep.clk = t.on ? h->clk : nullptr;
     HIPCHK(launch_gemm<E>(EPI_QKV, Xn, reinterpret_cast<const E*>(w.wqkv), n_qkv, d, rs.m_upper, rs.meta, ep, s));
   }
 
@@ -410,6 +414,7 @@ mor_status run_layer(mor_handle_s* h, const BlockPacked& w, float* X, const RowS
   er.xin = x_in;
   {
     TimedLaunch t(h, KIND_O, s);
+    er.clk = t.on ? h->clk : nullptr;
     HIPCHK(launch_gemm<E>(EPI_RESID, reinterpret_cast<const E*>(h->O), reinterpret_cast<const E*>(w.wo), d, h->nq, rs.m_upper, rs.meta, er, s));
   }
   er.xin = nullptr;
@@ -422,10 +427,12 @@ mor_status run_layer(mor_handle_s* h, const BlockPacked& w, float* X, const RowS
   eg.h = h->Hf; eg.ldh = dff;
   {
     TimedLaunch t(h, KIND_GATE_UP, s);
+    eg.clk = t.on ? h->clk : nullptr;
     HIPCHK(launch_gemm<E>(EPI_SWIGLU, Xn, reinterpret_cast<const E*>(w.wgu), 2 * dff, d, rs.m_upper, rs.meta, eg, s));
   }
   {
     TimedLaunch t(h, KIND_DOWN, s);
+    er.clk = t.on ? h->clk : nullptr;
     HIPCHK(launch_gemm<E>(EPI_RESID, reinterpret_cast<const E*>(h->Hf), reinterpret_cast<const E*>(w.wd), d, dff, rs.m_upper, rs.meta, er, s));
   }
   return MOR_OK;
@@ -978,6 +985,11 @@ mor_status mor_timing_enable(mor_handle* h, int32_t kind, int32_t max_launches) 
   h->ev.clear();
   h->ev_used = 0;
   h->timing_kind = kind;
+  if (h->clk) {
+    const unsigned long long zero[2] = {0, 0};
+    HIPCHK(hipDeviceSynchronize());
+    HIPCHK(hipMemcpy(h->clk, zero, sizeof(zero), hipMemcpyHostToDevice));
+  }
   if (kind == 0) return MOR_OK;
   h->ev.resize(2 * (size_t)max_launches, nullptr);
   for (auto& e : h->ev) HIPCHK(hipEventCreate(&e));
@@ -996,6 +1008,19 @@ mor_status mor_timing_read(mor_handle* h, double* total_ms, int32_t* launches) {
   *total_ms = acc;
   *launches = (int32_t)(h->ev_used / 2);
   h->ev_used = 0;
+  return MOR_OK;
+}
+
+mor_status mor_timing_clock(mor_handle* h, double* ghz) {
+  if (!h || !ghz) return fail(MOR_E_INVALID, "null pointer");
+  *ghz = 0.0;
+  if (!h->clk) return MOR_OK;
+  unsigned long long v[2] = {0, 0};
+  HIPCHK(hipDeviceSynchronize());
+  HIPCHK(hipMemcpy(v, h->clk, sizeof(v), hipMemcpyDeviceToHost));
+  int khz = 0;
+  HIPCHK(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, h->device));
+  if (v[1] > 0 && khz > 0) *ghz = (double)v[0] / (double)v[1] * (double)khz * 1e-6;
   return MOR_OK;
 }
 

@@ -27,6 +27,9 @@ struct GemmEpi {
   // host side: the launch's row count is only an upper bound (the rows are counted on the
   // device), so the tile choice avoids tiles of one workgroup per CU
   int rows_bound;
+  // measurement hook (bf16 kernel): when set, the first workgroup adds its shader cycles and
+  // real-time counter ticks over its life to clk[0] and clk[1]
+  unsigned long long* clk;
 };
 
 // Row-set descriptor ("meta"): meta[0] = total rows M, meta[1 + b] = first row of sequence b.

@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 PEAK_BF16 = 2.5e15          # dense MFMA bf16, FLOP/s (MI355X)
 PEAK_FP32 = 157.3e12
 PEAK_HBM = 8.0e12           # B/s
+PEAK_CLOCK_GHZ = 2.4        # shader clock the published peaks assume (256 CUs)
 KERNEL_SOURCES = {"gate_up": "adaptive_depth_recursive_amd/csrc/k_gemm_bf16.hip",
                   "qkv": "adaptive_depth_recursive_amd/csrc/k_gemm_bf16.hip",
                   "o_proj": "adaptive_depth_recursive_amd/csrc/k_gemm_bf16.hip",
@@ -471,6 +472,7 @@ def main():
     torch.cuda.synchronize()
     ms_ev = start.elapsed_time(end)
     k_ms, k_n = model.timing_read()
+    clock_ghz = model.timing_clock()
     model.timing_enable("", 0)
 
     step_s = ms / 1e3 / args.steps
@@ -490,8 +492,14 @@ def main():
                 "flops_per_launch": k_flops_per_launch,
                 "call_achieved": fl["total"] / step_s / 1e12,
                 "call_frac": fl["total"] / step_s / peak,
+                "clock_ghz": clock_ghz or None,
+                "peak_at_clock": (peak / 1e12 * clock_ghz / PEAK_CLOCK_GHZ) if clock_ghz else None,
+                "frac_at_clock": (achieved * 1e12 / (peak * clock_ghz / PEAK_CLOCK_GHZ)) if (clock_ghz and achieved) else None,
                 "note": "achieved/frac: the dominant kernel per launch; call_achieved/call_frac: the "
-                        "whole prefill call (all kernels, algorithmic FLOPs) against the same peak"}
+                        "whole prefill call (all kernels, algorithmic FLOPs) against the same peak; "
+                        "clock_ghz: shader clock during the kernel's timed launches (cycle counter "
+                        "against the real-time counter, first workgroup), peak_at_clock/frac_at_clock: "
+                        "the peak scaled from its 2.4 GHz to that clock"}
 
     # memory-bound kernels of the call: algorithmic bytes against HBM
     mem = {}

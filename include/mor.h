@@ -215,6 +215,12 @@ mor_status mor_get_error_flags(mor_handle* h, void* stream, uint32_t* flags);
  * the number of recorded launches, and clears the record. */
 mor_status mor_timing_enable(mor_handle* h, int32_t kind, int32_t max_launches);
 mor_status mor_timing_read(mor_handle* h, double* total_ms, int32_t* launches);
+/* Shader clock during the recorded launches of a bf16 projection kind (1, 3, 4, 5): each such
+ * launch's first workgroup counts shader cycles and constant-rate real-time ticks over its life;
+ * *ghz = cycles / ticks x the real-time rate, summed over the launches recorded since
+ * mor_timing_enable (which clears the sums), or 0 when none were sampled. Synchronises the
+ * device. */
+mor_status mor_timing_clock(mor_handle* h, double* ghz);
 
 /* ---------------------------------------------------------------- depth-wise batched decode
  * Continuous depth-wise batching (reading notes section 4) of the threshold-routed model (reading

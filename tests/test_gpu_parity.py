@@ -414,3 +414,26 @@ def test_prefill_without_optional_outputs(name):
         ref = oracle.prefill(cfg, W, H0[b:b + 1], forced_sel=fs)
         e = rel_err(plain[b], ref["out"][0])
         assert e <= tolerance(cfg), (b, e)
+
+
+def test_projection_timing_and_clock_sampling():
+    """The measurement hooks: events around every gate/up launch of a call, and the shader clock
+    sampled by those launches' first workgroup, within the chip's range; a kind without sampling
+    (attention) reports no clock."""
+    cfg = workload.get_config("small_bf16")
+    model, _ = build_gpu(cfg)
+    import torch
+    h = torch.from_numpy(workload.make_inputs(cfg)).cuda()
+    out = torch.empty_like(h)
+    model.timing_enable("gate_up", 64)
+    model.prefill(h, out)
+    ms, n = model.timing_read()
+    ghz = model.timing_clock()
+    assert n == cfg.n_layers and ms > 0, (n, ms)
+    assert 0.5 < ghz < 3.0, ghz
+    model.timing_enable("attention", 64)
+    model.prefill(h, out)
+    ms, n = model.timing_read()
+    assert n == cfg.n_layers and model.timing_clock() == 0.0
+    model.timing_enable("", 0)
+    model.close()

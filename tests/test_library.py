@@ -100,6 +100,7 @@ def test_null_handle_calls_rejected():
     assert L.mor_prefill(None, None, 1, 1, None, None, None, None, None, None) == mor.MOR_E_INVALID
     assert L.mor_route(None, None, None, None, 1, 1, 1, None, None, None, None) == mor.MOR_E_INVALID
     assert L.mor_route_noalloc(None, None, None, None, 1, 1, 1, None, None, None, None) == mor.MOR_E_INVALID
+    assert L.mor_timing_clock(None, None) == mor.MOR_E_INVALID
     L.mor_destroy(None)
 
 
