@@ -178,9 +178,9 @@ def decode_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def decode_traffic_from_profile():
-    """HBM-side bytes per decode iteration from the committed counter summary, if it was taken
-    on the current decode kernels and launch sequence (null otherwise)."""
+def decode_profile_record():
+    """The committed decode counter summary, if it was taken on the current decode kernels and
+    launch sequence (None otherwise)."""
     path = os.path.join(ROOT, "profiles", "decode_smol360m_mor4_traffic.json")
     if not os.path.exists(path):
         return None
@@ -188,7 +188,14 @@ def decode_traffic_from_profile():
         rec = json.load(f)
     if rec.get("source_sha256_16") != decode_source_hash():
         return None
-    return rec.get("bytes_per_iteration")
+    return rec
+
+
+def decode_traffic_from_profile():
+    """HBM-side bytes per decode iteration from the committed counter summary (null when it was
+    taken on other sources)."""
+    rec = decode_profile_record()
+    return rec.get("bytes_per_iteration") if rec else None
 
 
 def host_threads_and_cpu():
@@ -308,6 +315,8 @@ def decode_bench(args, kv_mode="recursion"):
         "roofline": {"bound": "hbm", "achieved": byt / s_ / 1e9 if s_ else None, "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": byt / s_ / PEAK_HBM if s_ else None,
                      "traffic": decode_traffic_from_profile() if kv_mode == "recursion" else None,
+                     "l2_hit_rate": ((decode_profile_record() or {}).get("l2_hit_rate")
+                                     if kv_mode == "recursion" else None),
                      "algorithmic_bytes_per_iteration": byt / max(it, 1),
                      "kv_read_bytes_per_iteration": kvr / max(it, 1)},
         "exit_depth_histogram": np.bincount(done, minlength=cfg.n_rec + 1)[1:].tolist(),
