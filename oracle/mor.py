@@ -363,7 +363,8 @@ def _prefill_one(cfg, W, h0, ks, forced, gate_mode, update):
             H[sel] = X
         elif cfg.routing == "tc":
             # Reading of the token-choice update: plain recursion before the chosen
-            # depth, gated delta at the chosen depth (parity unpinned).
+            # depth, gated delta at the chosen depth (pinned to a Llama stack combined
+            # by this rule; the rule itself is the reading).
             last = depth[sel] == r
             Hn = X.copy()
             Hn[last] = Hs[last] + g[last, None] * (X[last] - Hs[last])
